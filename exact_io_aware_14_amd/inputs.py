@@ -1,0 +1,84 @@
+"""Seeded synthetic inputs and the workload table.
+
+This module holds no attention arithmetic: it only draws random tensors and
+names shapes. Both the HIP path (tests, bench) and the fp64 oracle are fed
+from it, so the two sides see bit-identical inputs.
+
+Recipe: config k seeds ``torch.Generator('cpu').manual_seed(k)`` and draws, in
+this order, Q, K, V (then dO for a backward workload) with ``torch.randn`` in
+float32, i.i.d. N(0, 1); bf16 workloads round these draws to bf16 (round to
+nearest even) on the CPU. The oracle receives the same rounded values upcast
+exactly to float64.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    backward: bool
+    dtype: str          # "f32" (fp32 in/out, rounded to bf16 on load) or "bf16"
+    seed: int
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.d)
+
+
+# The five workloads the method is measured and checked on.
+WORKLOADS = [
+    Workload("fwd_b1h1n256d64_f32", 1, 1, 256, 64, False, False, "f32", 1),
+    Workload("fwd_b8h16n2048d64", 8, 16, 2048, 64, False, False, "bf16", 2),
+    Workload("fwd_causal_b4h32n4096d128", 4, 32, 4096, 128, True, False, "bf16", 3),
+    Workload("fwd_causal_b1h16n32768d128", 1, 16, 32768, 128, True, False, "bf16", 4),
+    Workload("fwdbwd_causal_b4h16n4096d128", 4, 16, 4096, 128, True, True, "bf16", 5),
+]
+
+
+def by_name(name: str) -> Workload:
+    for w in WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def draw(shape, seed, with_grad=False, dtype="bf16"):
+    """Return CPU tensors (q, k, v[, do]) drawn i.i.d. N(0,1) from ``seed``.
+
+    dtype "bf16": rounded to torch.bfloat16; "f32": left in float32.
+    """
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    names = ["q", "k", "v"] + (["do"] if with_grad else [])
+    out = []
+    for _ in names:
+        x = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+        if dtype == "bf16":
+            x = x.to(torch.bfloat16)
+        elif dtype != "f32":
+            raise ValueError(dtype)
+        out.append(x)
+    return tuple(out)
+
+
+def draw_workload(w: Workload):
+    return draw(w.shape, w.seed, with_grad=w.backward, dtype=w.dtype)
+
+
+def to_f64(x: torch.Tensor):
+    """Exact upcast of a CPU tensor to a float64 numpy array."""
+    return x.detach().to("cpu").to(torch.float64).numpy()

@@ -1,0 +1,293 @@
+"""Checks that pin the fp64 oracle to facts outside itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+what the pages or the mathematics fix. They look the oracle functions up on
+the module at call time, so tests/test_oracle_mutations.py can plant a
+mistake in the oracle and confirm that at least one pin catches it.
+
+Sources of truth used here, none of which is the oracle's own code:
+* hand-derived closed forms (tests/golden/closed_form.json);
+* torch's fp64 CPU scaled_dot_product_attention and autograd (a library);
+* central finite differences of the oracle's forward (for its backward);
+* pure-Python loops with math.exp on tiny inputs (brute force);
+* the blockwise online-softmax algorithm of the unite.ai page ("Dettagli di
+  Implementazione"), written here independently, with the old running sum
+  restored in the output update (the printed version omits it);
+* invariants of softmax attention (rows of P sum to 1, a single key returns
+  V, constant V returns that constant, zero queries give (prefix) means,
+  the merge identity over a split key set, shift and permutation behaviour,
+  and the gradient identities sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle.attention as A
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_form.json")
+
+
+def _close(x, y, tol, what):
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    assert x.shape == y.shape, f"{what}: shape {x.shape} vs {y.shape}"
+    err = np.max(np.abs(x - y)) if x.size else 0.0
+    assert np.all(np.isfinite(x)) and err <= tol, f"{what}: max abs err {err} > {tol}"
+
+
+def _rand_head(rng, n, d, nk=None):
+    nk = n if nk is None else nk
+    return (rng.standard_normal((n, d)), rng.standard_normal((nk, d)),
+            rng.standard_normal((nk, d)))
+
+
+# ---------------------------------------------------------------- golden
+
+def pin_golden_forward():
+    data = json.load(open(GOLDEN))
+    for case in data["cases"]:
+        o, lse = A.forward_head(np.array(case["q"]), np.array(case["k"]),
+                                np.array(case["v"]), case["scale"], case["causal"])
+        _close(o, case["o"], 1e-12, case["name"] + " O")
+        _close(lse, case["lse"], 1e-12, case["name"] + " lse")
+
+
+def pin_golden_backward():
+    data = json.load(open(GOLDEN))
+    for case in data["backward_cases"]:
+        q, k, v, do = (np.array(case[x]) for x in ("q", "k", "v", "do"))
+        o, _ = A.forward_head(q, k, v, case["scale"], case["causal"])
+        _close(o, case["o"], 1e-12, case["name"] + " O")
+        dq, dk, dv = A.backward_head(q, k, v, do, case["scale"], case["causal"])
+        _close(dq, case["dq"], 1e-12, case["name"] + " dQ")
+        _close(dk, case["dk"], 1e-12, case["name"] + " dK")
+        _close(dv, case["dv"], 1e-12, case["name"] + " dV")
+
+
+# ---------------------------------------------------------------- library
+
+SHAPES = [(1, 1), (2, 3), (5, 4), (17, 8), (33, 16), (64, 5)]
+
+
+def _torch_sdpa(q, k, v, scale, causal):
+    t = [torch.tensor(x, dtype=torch.float64)[None, None] for x in (q, k, v)]
+    if scale >= 0:
+        return torch.nn.functional.scaled_dot_product_attention(
+            *t, is_causal=causal, scale=scale)[0, 0].numpy()
+    # torch's fused path masks before scaling, which turns -inf into +inf for a
+    # negative scale; form the masked scores and call torch.softmax instead.
+    s = (t[0] @ t[1].transpose(-1, -2))[0, 0] * scale
+    if causal:
+        n = s.shape[0]
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), -math.inf)
+    return (torch.softmax(s, dim=-1) @ t[2][0, 0]).numpy()
+
+
+def pin_vs_torch_sdpa():
+    rng = np.random.default_rng(11)
+    for n, d in SHAPES:
+        for causal in (False, True):
+            for scale in (1.0 / math.sqrt(d), -0.7, 2.5):
+                q, k, v = _rand_head(rng, n, d)
+                o, lse = A.forward_head(q, k, v, scale, causal)
+                _close(o, _torch_sdpa(q, k, v, scale, causal), 1e-12,
+                       f"O vs torch n={n} d={d} causal={causal} scale={scale}")
+                s = torch.tensor(q) @ torch.tensor(k).T * scale
+                if causal:
+                    s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), -math.inf)
+                _close(lse, torch.logsumexp(s, dim=-1).numpy(), 1e-12,
+                       f"lse vs torch.logsumexp n={n} d={d}")
+
+
+def pin_backward_vs_autograd():
+    rng = np.random.default_rng(12)
+    for n, d in SHAPES:
+        for causal in (False, True):
+            scale = 1.0 / math.sqrt(d)
+            q, k, v = _rand_head(rng, n, d)
+            do = rng.standard_normal((n, d))
+            t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v)]
+            out = torch.nn.functional.scaled_dot_product_attention(
+                t[0][None, None], t[1][None, None], t[2][None, None],
+                is_causal=causal, scale=scale)[0, 0]
+            out.backward(torch.tensor(do))
+            dq, dk, dv = A.backward_head(q, k, v, do, scale, causal)
+            for name, mine, ref in (("dQ", dq, t[0].grad), ("dK", dk, t[1].grad),
+                                    ("dV", dv, t[2].grad)):
+                _close(mine, ref.numpy(), 1e-11, f"{name} vs autograd n={n} causal={causal}")
+
+
+# ---------------------------------------------------------------- finite differences
+
+def pin_finite_differences():
+    rng = np.random.default_rng(13)
+    eps = 1e-6
+    for n, d, causal in ((3, 2, False), (4, 3, True), (1, 2, True)):
+        scale = 0.8
+        q, k, v = _rand_head(rng, n, d)
+        do = rng.standard_normal((n, d))
+        grads = A.backward_head(q, k, v, do, scale, causal)
+
+        def loss(qq, kk, vv):
+            return float(np.sum(do * A.forward_head(qq, kk, vv, scale, causal)[0]))
+
+        for which in range(3):
+            base = [q, k, v]
+            num = np.zeros_like(base[which])
+            for idx in np.ndindex(*num.shape):
+                plus = [x.copy() for x in base]
+                minus = [x.copy() for x in base]
+                plus[which][idx] += eps
+                minus[which][idx] -= eps
+                num[idx] = (loss(*plus) - loss(*minus)) / (2 * eps)
+            _close(grads[which], num, 1e-7, f"finite differences input {which} n={n}")
+
+
+# ---------------------------------------------------------------- brute force
+
+def pin_brute_force():
+    rng = np.random.default_rng(14)
+    for n, d in ((1, 1), (3, 2), (6, 3)):
+        for causal in (False, True):
+            scale = 0.9
+            q, k, v = _rand_head(rng, n, d)
+            o, lse = A.forward_head(q, k, v, scale, causal)
+            for i in range(n):
+                keys = [j for j in range(n) if (j <= i or not causal)]
+                scores = [scale * sum(q[i][c] * k[j][c] for c in range(d)) for j in keys]
+                weights = [math.exp(s) for s in scores]
+                total = sum(weights)
+                for c in range(d):
+                    ref = sum(w * v[j][c] for w, j in zip(weights, keys)) / total
+                    assert abs(o[i][c] - ref) <= 1e-12, ("brute O", n, i, c)
+                assert abs(lse[i] - math.log(total)) <= 1e-12, ("brute lse", n, i)
+
+
+# ---------------------------------------------------------------- online recurrence
+
+def online_blockwise(q, k, v, scale, causal, block):
+    """Blockwise attention with a running max and sum, Q blocks outer, K/V inner.
+
+    Follows the steps of the unite.ai page's simplified implementation, with
+    the output update written as O <- (e^(m-m_new) * l_old * O + P V) / l_new,
+    i.e. with the old running sum restored, which the printed code omits.
+    """
+    n = q.shape[0]
+    out = np.zeros((n, v.shape[1]))
+    run_l = np.zeros(n)
+    run_m = np.full(n, -np.inf)
+    for i0 in range(0, n, block):
+        rows = np.arange(i0, min(n, i0 + block))
+        for j0 in range(0, k.shape[0], block):
+            cols = np.arange(j0, min(k.shape[0], j0 + block))
+            s = scale * (q[rows] @ k[cols].T)
+            if causal:
+                s = np.where(cols[None, :] <= rows[:, None], s, -np.inf)
+            m_new = np.maximum(run_m[rows], s.max(axis=1))
+            live = np.isfinite(m_new)
+            m_use = np.where(live, m_new, 0.0)
+            p = np.exp(s - m_use[:, None])
+            alpha = np.where(np.isfinite(run_m[rows]), np.exp(run_m[rows] - m_use), 0.0)
+            l_new = alpha * run_l[rows] + p.sum(axis=1)
+            safe = np.where(l_new > 0, l_new, 1.0)
+            out[rows] = ((alpha * run_l[rows])[:, None] * out[rows] + p @ v[cols]) / safe[:, None]
+            run_l[rows] = l_new
+            run_m[rows] = np.where(live, m_new, run_m[rows])
+    return out, run_m + np.log(run_l)
+
+
+def pin_online_recurrence():
+    rng = np.random.default_rng(15)
+    for n, d, block in ((64, 8, 16), (50, 4, 7), (130, 16, 32)):
+        for causal in (False, True):
+            q, k, v = _rand_head(rng, n, d)
+            q *= 3.0  # peaked rows: the running max moves between blocks
+            o, lse = A.forward_head(q, k, v, 0.5, causal)
+            o2, lse2 = online_blockwise(q, k, v, 0.5, causal, block)
+            _close(o, o2, 1e-12, f"online recurrence O n={n} block={block}")
+            _close(lse, lse2, 1e-12, f"online recurrence lse n={n}")
+
+
+# ---------------------------------------------------------------- invariants
+
+def pin_forward_invariants():
+    rng = np.random.default_rng(16)
+    n, d = 40, 6
+    for causal in (False, True):
+        q, k, v = _rand_head(rng, n, d)
+        scale = 0.6
+        # rows of P sum to one
+        p = A.probabilities_head(q, k, scale, causal)
+        _close(p.sum(axis=1), np.ones(n), 1e-12, "P row sums")
+        if causal:
+            assert np.all(np.triu(p, 1) == 0.0), "causal P has mass above the diagonal"
+        # constant V returns the constant
+        cv = np.tile(rng.standard_normal(d), (n, 1))
+        _close(A.forward_head(q, k, cv, scale, causal)[0], cv, 1e-12, "constant V")
+        # zero queries: (prefix) means, lse = ln(count)
+        o0, l0 = A.forward_head(np.zeros_like(q), k, v, scale, causal)
+        if causal:
+            means = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+            counts = np.arange(1, n + 1)
+        else:
+            means = np.tile(v.mean(axis=0), (n, 1))
+            counts = np.full(n, n)
+        _close(o0, means, 1e-12, "zero query means")
+        _close(l0, np.log(counts), 1e-12, "zero query lse")
+        # key shift: O unchanged, lse shifts by scale * q.c
+        c = rng.standard_normal(d)
+        o, lse = A.forward_head(q, k, v, scale, causal)
+        o_s, lse_s = A.forward_head(q, k + c, v, scale, causal)
+        _close(o_s, o, 1e-11, "key shift O")
+        _close(lse_s, lse + scale * (q @ c), 1e-11, "key shift lse")
+    # single key returns V exactly
+    q, k, v = _rand_head(rng, 5, d, nk=1)
+    o, lse = A.forward_head(q, k, v, 1.3, False)
+    _close(o, np.tile(v, (5, 1)), 0.0, "single key")
+    _close(lse, 1.3 * (q @ k[0]), 1e-12, "single key lse")
+    # joint permutation of K and V rows (non-causal) leaves O unchanged
+    q, k, v = _rand_head(rng, 30, d)
+    perm = rng.permutation(30)
+    _close(A.forward_head(q, k[perm], v[perm], 0.4, False)[0],
+           A.forward_head(q, k, v, 0.4, False)[0], 1e-12, "permutation")
+    # split the key set in two and merge the partial results
+    q, k, v = _rand_head(rng, 24, d, nk=50)
+    q *= 4.0
+    o, lse = A.forward_head(q, k, v, 0.7, False)
+    o1, l1 = A.forward_head(q, k[:13], v[:13], 0.7, False)
+    o2, l2 = A.forward_head(q, k[13:], v[13:], 0.7, False)
+    om, lm = A.merge(o1, l1, o2, l2)
+    _close(om, o, 1e-12, "merge O")
+    _close(lm, lse, 1e-12, "merge lse")
+
+
+def pin_backward_invariants():
+    rng = np.random.default_rng(17)
+    n, d = 30, 5
+    for causal in (False, True):
+        q, k, v = _rand_head(rng, n, d)
+        do = rng.standard_normal((n, d))
+        dq, dk, dv = A.backward_head(q, k, v, do, 0.5, causal)
+        # softmax is invariant to shifting all keys: the key gradients sum to zero
+        _close(dk.sum(axis=0), np.zeros(d), 1e-11, "sum dK")
+        # each row of P sums to one: the value gradients sum to the sum of dO
+        _close(dv.sum(axis=0), do.sum(axis=0), 1e-11, "sum dV")
+        # identical keys: scores do not depend on q, so dQ = 0
+        kk = np.tile(k[:1], (n, 1))
+        dq0, _, _ = A.backward_head(q, kk, v, do, 0.5, causal)
+        _close(dq0, np.zeros_like(dq0), 1e-12, "identical keys dQ")
+        # D_i = sum_k dO_ik O_ik equals sum_j P_ij dP_ij
+        p = A.probabilities_head(q, k, 0.5, causal)
+        o = A.forward_head(q, k, v, 0.5, causal)[0]
+        _close((do * o).sum(axis=1), (p * (do @ v.T)).sum(axis=1), 1e-11, "D identity")
+
+
+ALL_PINS = [pin_golden_forward, pin_golden_backward, pin_vs_torch_sdpa,
+            pin_backward_vs_autograd, pin_finite_differences, pin_brute_force,
+            pin_online_recurrence, pin_forward_invariants, pin_backward_invariants]
