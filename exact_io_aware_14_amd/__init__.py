@@ -1,0 +1,155 @@
+"""Exact tiled attention on MI355X (gfx950): Python binding of libfa.so.
+
+The functions here carry the names of the C ABI in include/fa.h and only
+marshal arguments: they check torch tensors (device, dtype, contiguity,
+shape), allocate missing outputs with torch, and pass raw device pointers and
+the current HIP stream to the library. Every step of the computation runs in
+the library's HIP kernels; there is no fallback. If libfa.so has not been
+built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["FAError", "fa_forward", "fa_forward_f32", "fa_backward",
+           "fa_backward_workspace_size", "fa_strerror", "library", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status}: {fa_strerror(status)}")
+        self.status = status
+
+
+def library():
+    """The loaded libfa.so (ctypes). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_14_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_forward.restype = i
+        lib.fa_forward_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_forward_f32.restype = i
+        lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
+        lib.fa_backward_workspace_size.restype = sz
+        lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
+                                    vp, sz, vp]
+        lib.fa_backward.restype = i
+        lib.fa_strerror.argtypes = [i]
+        lib.fa_strerror.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def fa_strerror(status: int) -> str:
+    return library().fa_strerror(int(status)).decode()
+
+
+def fa_backward_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(library().fa_backward_workspace_size(B, H, N, d))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on {device} (a HIP device)")
+
+
+def _forward(fn_name, q, k, v, scale, causal, o, lse, stream, dtype):
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, dtype, (B, H, N, d), dev)
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check(o, "o", dtype, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    if scale is None:
+        scale = d ** -0.5
+    st = getattr(library(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                     B, H, N, d, float(scale), int(bool(causal)),
+                                     _stream(stream))
+    if st != 0:
+        raise FAError(st, fn_name)
+    return o, lse
+
+
+def fa_forward(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None):
+    """O, lse = attention of bf16 [B,H,N,d] tensors (see fa_forward in fa.h)."""
+    return _forward("fa_forward", q, k, v, scale, causal, o, lse, stream,
+                    _torch().bfloat16)
+
+
+def fa_forward_f32(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None):
+    """fp32 in/out variant: inputs are rounded to bf16 as they are loaded."""
+    return _forward("fa_forward_f32", q, k, v, scale, causal, o, lse, stream,
+                    _torch().float32)
+
+
+def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
+                workspace=None, stream=None):
+    """dQ, dK, dV of sum(dout * O) (see fa_backward in fa.h)."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    bf = torch.bfloat16
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check(t, name, bf, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, bf, (B, H, N, d), dev)
+    need = fa_backward_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev:
+        raise ValueError("workspace must be on the same device")
+    if scale is None:
+        scale = d ** -0.5
+    st = library().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                               int(bool(causal)), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_backward")
+    return dq, dk, dv

@@ -1,0 +1,105 @@
+// C ABI of libfa.so: argument validation, then kernel launches on the
+// caller's stream. Declarations and the contract are in include/fa.h.
+#include "fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_launch.h"
+
+namespace {
+
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by the forward and backward entry points, in the order
+// documented in fa.h. Returns FA_OK and sets *empty when there is nothing to
+// compute.
+int check_common(int B, int H, int N, int d, float scale, int causal, bool* empty) {
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!isfinite(scale)) return FA_ERR_ARG;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  *empty = (B == 0 || H == 0 || N == 0);
+  if (*empty) return FA_OK;
+  if (fa::forward_grid_size(B, H, N) > kMaxGrid) return FA_ERR_SHAPE;
+  if (fa::backward_grid_size(B, H, N) > kMaxGrid) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_ptrs(const void* const* ptrs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (ptrs[i] == nullptr) return FA_ERR_NULL;
+  for (int i = 0; i < n; ++i)
+    if (!aligned16(ptrs[i])) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+int forward_common(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int N, int d, float scale, int causal, hipStream_t stream,
+                   bool f32) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  const void* ptrs[5] = {q, k, v, o, lse};
+  st = check_ptrs(ptrs, 5);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal, stream};
+  hipError_t e = f32 ? fa::launch_forward_f32(a) : fa::launch_forward_bf16(a);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, hipStream_t stream) {
+  return forward_common(q, k, v, o, lse, B, H, N, d, scale, causal, stream, false);
+}
+
+int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                   int H, int N, int d, float scale, int causal, hipStream_t stream) {
+  return forward_common(q, k, v, o, lse, B, H, N, d, scale, causal, stream, true);
+}
+
+size_t fa_backward_workspace_size(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                float scale, int causal, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
+  st = check_ptrs(ptrs, 9);
+  if (st != FA_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < fa_backward_workspace_size(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace),
+                B, H, N, d, scale, causal, stream};
+  hipError_t e = fa::launch_backward(a);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape: B, H or N negative, or the launch grid is too large";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
+    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case FA_ERR_ARG: return "invalid argument: causal must be 0 or 1 and scale finite";
+    case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

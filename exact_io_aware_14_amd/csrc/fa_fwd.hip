@@ -1,0 +1,355 @@
+// Forward exact attention for gfx950: one workgroup per (batch, head, block
+// of 128 query rows), four waves of 32 query rows each.
+//
+// Method: the tiled forward with a running row maximum m and row sum l, in
+// which the partial output of earlier key tiles is rescaled whenever m grows
+// ("Flash Attention: Rivoluzionando l'Efficienza dei Modelli Transformer"
+// (unite.ai), sections "L'Algoritmo di Flash Attention" and "La Matematica
+// dietro Flash Attention", formulas 1-2; "Attenzione flash"
+// (aiunderstanding.org), "Approfondimento tecnico"). The work decomposition
+// is the FlashAttention-2 one described on the nearauto.com article
+// (section "より優れた並列処理": one worker per row block of the attention
+// matrix; section "より良い作業分割": the query rows are split across the
+// waves and every wave sees the whole K/V tile, so waves never exchange
+// partial results). The normalisation by l happens once at the end, and the
+// output is rescaled only when a row maximum has grown by more than 2^8
+// (section "非matmul FLOPの減少": fewer non-matmul operations).
+//
+// Per wave and key tile (BC keys) the kernel computes the transposed score
+// tile S^T = K Q^T on MFMA, so that each lane owns one query row (column c of
+// the accumulator) and holds 16 of the tile's scores per 32 keys; the two
+// halves of the wave hold the other keys of the same rows. The probabilities
+// are packed to bf16 in the lane and feed the product O^T += V^T P^T
+// directly as its B operand; V is kept transposed in LDS to serve as the A
+// operand.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 32;
+constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
+constexpr int kBC = 64;                     // keys per tile
+constexpr int kThreads = kWaves * 64;
+// A row maximum may exceed the reference used for the exponentials by up to
+// this many powers of two before the accumulators are rescaled; the
+// probabilities then stay below 2^8, far inside fp32 and bf16 range.
+constexpr float kRescaleSlack = 8.0f;
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int BH;        // batch * heads
+  int N;         // sequence length
+  int nqb;       // query blocks per head
+  float c;       // |scale| * log2(e)
+  int negate_q;  // scale < 0: Q is negated on load and |scale| is used
+  int xcd_remap; // heads grouped per XCD (requires BH % 8 == 0)
+};
+
+// Position of key `key` inside a transposed V row of the tile: bits 2 and 3
+// of the key index are swapped, so that the eight keys one lane needs for
+// one P.V product are contiguous (see the S^T accumulator layout).
+__device__ __forceinline__ int vt_pos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+template <int D>
+struct Smem {
+  uint16_t k[kBC * D];   // K tile, row-major [key][d], 16-byte chunks XOR-swizzled by row
+  uint16_t vt[D * kBC];  // V tile transposed [d][pos(key)], chunks swizzled by d
+};
+
+template <int D, typename TIn>
+struct TileLoader {
+  static constexpr int kChunks = D / 8;                       // 16-byte chunks per row
+  static constexpr int kKLoads = kBC * kChunks / kThreads;    // K chunks per thread
+  static constexpr int kVGroups = (kBC / 4) * kChunks;        // (4-key group, chunk) pairs
+  static constexpr int kVLoads = (kVGroups + kThreads - 1) / kThreads;
+  static_assert(kBC * kChunks % kThreads == 0, "K tile must split evenly");
+
+  uint4 kreg[kKLoads];
+  uint4 vreg[kVLoads][4];
+
+  __device__ __forceinline__ void load(const TIn* kbase, const TIn* vbase, int key0, int N,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) {
+      int id = tid + i * kThreads;
+      int row = id / kChunks, ch = id % kChunks;
+      int key = key0 + row;
+      bool ok = key < N;
+      kreg[i] = load8<TIn>(kbase + (size_t)(ok ? key : 0) * D + ch * 8, ok);
+    }
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i) {
+      int id = tid + i * kThreads;
+      int ch = id % kChunks, g = id / kChunks;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int key = key0 + 4 * g + r;
+        bool ok = (id < kVGroups) && key < N;
+        vreg[i][r] = load8<TIn>(vbase + (size_t)(ok ? key : 0) * D + ch * 8, ok);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(Smem<D>& sm, int tid) {
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) {
+      int id = tid + i * kThreads;
+      int row = id / kChunks, ch = id % kChunks;
+      *reinterpret_cast<uint4*>(&sm.k[row * D + ((ch ^ (row & 7)) * 8)]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i) {
+      int id = tid + i * kThreads;
+      if (id < kVGroups) {
+        int ch = id % kChunks, g = id / kChunks;
+        int pos = vt_pos(4 * g);  // the four keys stay adjacent: bits 0-1 unchanged
+        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
+        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
+        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
+        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // d = ch*8 + 2j (low halves) and d + 1 (high halves)
+          uint2 lo, hi;
+          lo.x = (w0[j] & 0xffffu) | (w1[j] << 16);
+          lo.y = (w2[j] & 0xffffu) | (w3[j] << 16);
+          hi.x = (w0[j] >> 16) | (w1[j] & 0xffff0000u);
+          hi.y = (w2[j] >> 16) | (w3[j] & 0xffff0000u);
+          int d0 = ch * 8 + 2 * j;
+          int d1 = d0 + 1;
+          *reinterpret_cast<uint2*>(&sm.vt[d0 * kBC + (((pos >> 3) ^ (d0 & 7)) * 8) + (pos & 7)]) = lo;
+          *reinterpret_cast<uint2*>(&sm.vt[d1 * kBC + (((pos >> 3) ^ (d1 & 7)) * 8) + (pos & 7)]) = hi;
+        }
+      }
+    }
+  }
+};
+
+template <int D, bool CAUSAL, typename TIn, typename TOut>
+__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
+  __shared__ Smem<D> sm;
+  constexpr int kDK = D / 16;  // MFMA steps along d for S^T
+  constexpr int kDB = D / 32;  // 32-row blocks of O^T
+  constexpr int kKB = kBC / 32;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // ---- which (head, query block) this workgroup owns
+  int bh, qbr;
+  const int L = blockIdx.x;
+  if (p.xcd_remap) {
+    // consecutive workgroups go to the 8 XCDs in turn; give each XCD whole
+    // heads so the K/V of a head is re-read from that XCD's L2
+    int xcd = L & 7, idx = L >> 3;
+    bh = (idx / p.nqb) * 8 + xcd;
+    qbr = idx % p.nqb;
+  } else {
+    bh = L % p.BH;
+    qbr = L / p.BH;
+  }
+  // causal: the longest rows (most key tiles) are dispatched first
+  const int qb = CAUSAL ? (p.nqb - 1 - qbr) : qbr;
+  const int N = p.N;
+  const size_t head_off = (size_t)bh * (size_t)N * D;
+  const TIn* qg = reinterpret_cast<const TIn*>(p.q) + head_off;
+  const TIn* kg = reinterpret_cast<const TIn*>(p.k) + head_off;
+  const TIn* vg = reinterpret_cast<const TIn*>(p.v) + head_off;
+
+  const int q0 = qb * kBR;                        // first row of the block
+  const int qw0 = q0 + wave * kRowsPerWave;       // first row of this wave
+  const int myq = qw0 + col;                      // this lane's row
+  const int wave_last = min(qw0 + kRowsPerWave, N) - 1;
+
+  // ---- Q^T as the B operand of S^T = K Q^T: column = row myq, k-slots = d
+  bf16x8 qreg[kDK];
+#pragma unroll
+  for (int kk = 0; kk < kDK; ++kk) {
+    bool ok = myq < N;
+    uint4 u = load8<TIn>(qg + (size_t)(ok ? myq : 0) * D + kk * 16 + half * 8, ok);
+    if (p.negate_q) u = negate8(u);
+    qreg[kk] = as_bf16x8(u);
+  }
+
+  f32x16 oacc[kDB];
+#pragma unroll
+  for (int i = 0; i < kDB; ++i) oacc[i] = zero16();
+  float m_run = -INFINITY;  // reference maximum, in units of log2 (scale*log2e*score)
+  float l_run = 0.0f;       // this lane's part of the row sum
+
+  const int ktiles_all = (N + kBC - 1) / kBC;
+  const int ktiles = CAUSAL ? min(ktiles_all, (min(q0 + kBR, N) - 1) / kBC + 1) : ktiles_all;
+  const float c = p.c;
+
+  TileLoader<D, TIn> ld;
+  ld.load(kg, vg, 0, N, tid);
+
+  for (int t = 0; t < ktiles; ++t) {
+    __syncthreads();  // every wave is done reading the previous tile
+    ld.store(sm, tid);
+    __syncthreads();
+    if (t + 1 < ktiles) ld.load(kg, vg, (t + 1) * kBC, N, tid);
+
+    const int key0 = t * kBC;
+    if (CAUSAL && key0 > wave_last) continue;  // no visible key for this wave
+
+    // ---- S^T = K Q^T for the BC keys of the tile
+    f32x16 s[kKB];
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+      s[kb] = zero16();
+      const int row = kb * 32 + col;
+#pragma unroll
+      for (int kk = 0; kk < kDK; ++kk) {
+        const int ch = 2 * kk + half;
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[row * D + ((ch ^ (row & 7)) * 8)]);
+        s[kb] = mfma32(a, qreg[kk], s[kb]);
+      }
+    }
+
+    // ---- masks: keys past N, and keys after the row for causal
+    const bool need_mask = (key0 + kBC > N) || (CAUSAL && key0 + kBC - 1 > qw0);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          bool vis = key < N && (!CAUSAL || key <= myq);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+        }
+    }
+
+    // ---- row maximum over the tile (own 16*KB keys, then the other half)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float cand = (mx == -INFINITY) ? -INFINITY : mx * c;
+
+    // ---- move the reference maximum only when it is exceeded by the slack
+    const bool grow = cand > m_run + kRescaleSlack;
+    if (__any(grow)) {
+      const float m_new = fmaxf(m_run, cand);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < kDB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+
+    // ---- probabilities p = 2^(c*s - m), summed and packed to bf16
+    uint32_t pk[kKB][8];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        e[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+        if (need_mask) e[r] = (s[kb][r] == -INFINITY) ? 0.0f : e[r];
+        lsum += e[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) pk[kb][r] = pack_bf16x2(e[2 * r], e[2 * r + 1]);
+    }
+    l_run += lsum;
+
+    // ---- O^T += V^T P^T; P^T slots (kb, m) are accumulator rows 8m..8m+7
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        uint4 bu = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
+        const bf16x8 b = as_bf16x8(bu);
+        const int chunk = 4 * kb + 2 * m + half;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const int drow = db * 32 + col;
+          bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              &sm.vt[drow * kBC + ((chunk ^ (drow & 7)) * 8)]);
+          oacc[db] = mfma32(a, b, oacc[db]);
+        }
+      }
+  }
+
+  // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2
+  const float l_tot = l_run + swap_halves(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (myq < N) {
+    TOut* og = reinterpret_cast<TOut*>(p.o) + head_off + (size_t)myq * D;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * half;
+        float x0 = oacc[db][4 * g] * inv, x1 = oacc[db][4 * g + 1] * inv;
+        float x2 = oacc[db][4 * g + 2] * inv, x3 = oacc[db][4 * g + 3] * inv;
+        if constexpr (sizeof(TOut) == 2) {
+          uint2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+          *reinterpret_cast<uint2*>(og + d0) = w;
+        } else {
+          *reinterpret_cast<float4*>(og + d0) = make_float4(x0, x1, x2, x3);
+        }
+      }
+    if (half == 0) {
+      p.lse[(size_t)bh * N + myq] =
+          l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int D, bool CAUSAL, typename TIn, typename TOut>
+hipError_t launch_typed(const FwdArgs& a) {
+  FwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.BH = a.B * a.H;
+  p.N = a.N;
+  p.nqb = (a.N + kBR - 1) / kBR;
+  p.c = fabsf(a.scale) * kLog2e;
+  p.negate_q = a.scale < 0.0f;
+  p.xcd_remap = (p.BH % 8) == 0;
+  dim3 grid((unsigned)((long long)p.BH * p.nqb));
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, TIn, TOut>), grid, dim3(kThreads), 0, a.stream, p);
+  return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_dtype(const FwdArgs& a) {
+  if (a.d == 64) {
+    return a.causal ? launch_typed<64, true, TIn, TOut>(a) : launch_typed<64, false, TIn, TOut>(a);
+  }
+  return a.causal ? launch_typed<128, true, TIn, TOut>(a) : launch_typed<128, false, TIn, TOut>(a);
+}
+
+}  // namespace
+
+hipError_t launch_forward_bf16(const FwdArgs& a) { return launch_dtype<uint16_t, uint16_t>(a); }
+hipError_t launch_forward_f32(const FwdArgs& a) { return launch_dtype<float, float>(a); }
+
+long long forward_grid_size(int B, int H, int N) {
+  return (long long)B * H * ((N + kBR - 1) / kBR);
+}
+
+}  // namespace fa

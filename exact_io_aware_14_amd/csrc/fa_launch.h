@@ -1,0 +1,47 @@
+// Host-side launch interface between the C ABI (fa_api.hip) and the kernel
+// translation units. Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* drow;  // workspace: D_i = sum_k dO_ik O_ik, [B,H,N] fp32
+  int B, H, N, d;
+  float scale;
+  int causal;
+  hipStream_t stream;
+};
+
+hipError_t launch_forward_bf16(const FwdArgs& a);
+hipError_t launch_forward_f32(const FwdArgs& a);
+hipError_t launch_backward(const BwdArgs& a);
+
+// Workgroups the forward launch uses (for grid-size validation).
+long long forward_grid_size(int B, int H, int N);
+long long backward_grid_size(int B, int H, int N);
+
+}  // namespace fa

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects invalid arguments with the documented status before any HIP call."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_14_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_ARG, \
+    FA_ERR_WORKSPACE, FA_ERR_HIP = range(8)
+
+
+def declared_functions():
+    names = []
+    for path in HEADERS:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \*]*?\b(fa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail(f"{fa.LIB_PATH} not built: run python -m exact_io_aware_14_amd.build")
+    return fa.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_workspace_size",
+            "fa_strerror"} <= set(names)
+    raw = ctypes.CDLL(fa.LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), f"{name} declared in include/ but not exported"
+
+
+def test_strerror(lib):
+    for code in range(8):
+        s = fa.fa_strerror(code)
+        assert isinstance(s, str) and s
+    assert fa.fa_strerror(0) == "success"
+    assert fa.fa_strerror(99) == "unknown status"
+
+
+def test_workspace_size(lib):
+    assert fa.fa_backward_workspace_size(4, 16, 4096, 128) == 4 * 16 * 4096 * 4
+    assert fa.fa_backward_workspace_size(1, 1, 1, 64) == 4
+    assert fa.fa_backward_workspace_size(0, 1, 1, 64) == 0
+    assert fa.fa_backward_workspace_size(1, 1, 1, 96) == 0
+    assert fa.fa_backward_workspace_size(1, 1, -5, 64) == 0
+
+
+# Fake but aligned device addresses: validation must reject the call before
+# it would ever touch them.
+P = ctypes.c_void_p(0x10000)
+PM = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+NULL = ctypes.c_void_p(0)
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=64, scale=0.125, causal=0, f32=False):
+    fn = lib.fa_forward_f32 if f32 else lib.fa_forward
+    return fn(q, k, v, o, lse, B, H, N, d, scale, causal, NULL)
+
+
+def bwd(lib, ws=P, ws_bytes=None, d=64, B=1, H=1, N=16, causal=0, scale=0.125, ptrs=None):
+    ptrs = ptrs or [P] * 9
+    if ws_bytes is None:
+        ws_bytes = B * H * N * 4 if min(B, H, N) > 0 else 0
+    return lib.fa_backward(*ptrs, B, H, N, d, scale, causal, ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_forward_validation(lib, f32):
+    assert fwd(lib, causal=2, f32=f32) == FA_ERR_ARG
+    assert fwd(lib, causal=-1, f32=f32) == FA_ERR_ARG
+    assert fwd(lib, scale=float("nan"), f32=f32) == FA_ERR_ARG
+    assert fwd(lib, scale=float("inf"), f32=f32) == FA_ERR_ARG
+    for d in (0, 32, 96, 256, -64):
+        assert fwd(lib, d=d, f32=f32) == FA_ERR_HEADDIM
+    assert fwd(lib, B=-1, f32=f32) == FA_ERR_SHAPE
+    assert fwd(lib, H=-2, f32=f32) == FA_ERR_SHAPE
+    assert fwd(lib, N=-3, f32=f32) == FA_ERR_SHAPE
+    # the grid would not fit a launch
+    assert fwd(lib, B=2**20, H=2**10, N=2**16, f32=f32) == FA_ERR_SHAPE
+    for i in range(5):
+        args = [P] * 5
+        args[i] = NULL
+        assert fwd(lib, *args, f32=f32) == FA_ERR_NULL
+        args[i] = PM
+        assert fwd(lib, *args, f32=f32) == FA_ERR_ALIGN
+    # empty problems are a successful no-op, null pointers allowed
+    assert fwd(lib, NULL, NULL, NULL, NULL, NULL, B=0, f32=f32) == FA_OK
+    assert fwd(lib, NULL, NULL, NULL, NULL, NULL, H=0, f32=f32) == FA_OK
+    assert fwd(lib, NULL, NULL, NULL, NULL, NULL, N=0, f32=f32) == FA_OK
+
+
+def test_backward_validation(lib):
+    assert bwd(lib, causal=3) == FA_ERR_ARG
+    assert bwd(lib, scale=float("-inf")) == FA_ERR_ARG
+    assert bwd(lib, d=80) == FA_ERR_HEADDIM
+    assert bwd(lib, N=-1) == FA_ERR_SHAPE
+    for i in range(9):
+        ptrs = [P] * 9
+        ptrs[i] = NULL
+        assert bwd(lib, ptrs=ptrs) == FA_ERR_NULL
+        ptrs[i] = PM
+        assert bwd(lib, ptrs=ptrs) == FA_ERR_ALIGN
+    assert bwd(lib, ws=NULL) == FA_ERR_WORKSPACE
+    assert bwd(lib, ws=PM) == FA_ERR_WORKSPACE
+    assert bwd(lib, ws_bytes=16 * 4 - 1) == FA_ERR_WORKSPACE
+    assert bwd(lib, ptrs=[NULL] * 9, ws=NULL, N=0) == FA_OK
+
+
+def test_python_binding_without_gpu_raises_cleanly(lib):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_forward(q, q, q)  # CPU tensors are refused before the library is called
