@@ -91,4 +91,67 @@ __device__ __forceinline__ float swap_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// LDS tiles. A tile of R rows x D columns of bf16 is kept in one of two forms:
+//
+// * row-major [row][d]: the 16-byte chunk c of row r sits at chunk position
+//   c ^ (r & 7), so that the 32 lanes that read one chunk column of 32
+//   consecutive rows (an MFMA A or B operand) hit different banks;
+// * transposed [d][pos(row)]: each LDS row holds one column d of the tile.
+//   Rows are stored at position pos(r), r with bits 2 and 3 swapped, which
+//   makes the eight rows one lane needs for one MFMA operand (see below)
+//   contiguous; chunks are swizzled by d & 7 in the same way.
+//
+// Why the swap: an accumulator element r of the 32x32 MFMA covers row
+// 8*(r/4) + 4h + (r%4) of its 32-row block. Repacking accumulator elements
+// 8m .. 8m+7 of a lane as the operand slots of one 16-deep MFMA makes slot s
+// stand for row 16m + 8*(s/4) + 4h + (s%4); with bits 2 and 3 swapped that
+// is position 16m + 8h + s, one 16-byte chunk per lane.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int tpos(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Store chunk `ch` (8 elements) of row `row` into a row-major tile of width D.
+template <int D>
+__device__ __forceinline__ void st_row(uint16_t* tile, int row, int ch, uint4 val) {
+  *reinterpret_cast<uint4*>(&tile[row * D + ((ch ^ (row & 7)) * 8)]) = val;
+}
+
+// MFMA operand read: chunk `ch` of row `row` of a row-major tile.
+template <int D>
+__device__ __forceinline__ bf16x8 ld_row(const uint16_t* tile, int row, int ch) {
+  return *reinterpret_cast<const bf16x8*>(&tile[row * D + ((ch ^ (row & 7)) * 8)]);
+}
+
+// Store four consecutive rows r0..r0+3 (r0 % 4 == 0) of chunk `ch` (columns
+// 8ch..8ch+7) into a transposed tile of R rows: eight 8-byte writes.
+template <int R>
+__device__ __forceinline__ void st_tr4(uint16_t* tile, int r0, int ch, const uint4 w[4]) {
+  const int pos = tpos(r0);  // the four rows stay adjacent: bits 0-1 unchanged
+  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&w[0]);
+  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&w[1]);
+  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&w[2]);
+  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&w[3]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint2 lo, hi;  // column 8ch+2j from the low halves, 8ch+2j+1 from the high halves
+    lo.x = (w0[j] & 0xffffu) | (w1[j] << 16);
+    lo.y = (w2[j] & 0xffffu) | (w3[j] << 16);
+    hi.x = (w0[j] >> 16) | (w1[j] & 0xffff0000u);
+    hi.y = (w2[j] >> 16) | (w3[j] & 0xffff0000u);
+    const int d0 = ch * 8 + 2 * j, d1 = d0 + 1;
+    *reinterpret_cast<uint2*>(&tile[d0 * R + (((pos >> 3) ^ (d0 & 7)) * 8) + (pos & 7)]) = lo;
+    *reinterpret_cast<uint2*>(&tile[d1 * R + (((pos >> 3) ^ (d1 & 7)) * 8) + (pos & 7)]) = hi;
+  }
+}
+
+// MFMA operand read from a transposed tile of R rows: column `d`, positions
+// 8*chunk .. 8*chunk+7.
+template <int R>
+__device__ __forceinline__ bf16x8 ld_tr(const uint16_t* tile, int d, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(&tile[d * R + ((chunk ^ (d & 7)) * 8)]);
+}
+
 }  // namespace fa

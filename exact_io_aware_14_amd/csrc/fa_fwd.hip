@@ -52,17 +52,10 @@ struct FwdParams {
   int xcd_remap; // heads grouped per XCD (requires BH % 8 == 0)
 };
 
-// Position of key `key` inside a transposed V row of the tile: bits 2 and 3
-// of the key index are swapped, so that the eight keys one lane needs for
-// one P.V product are contiguous (see the S^T accumulator layout).
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
-
 template <int D>
 struct Smem {
-  uint16_t k[kBC * D];   // K tile, row-major [key][d], 16-byte chunks XOR-swizzled by row
-  uint16_t vt[D * kBC];  // V tile transposed [d][pos(key)], chunks swizzled by d
+  uint16_t k[kBC * D];   // K tile, row-major
+  uint16_t vt[D * kBC];  // V tile, transposed
 };
 
 template <int D, typename TIn>
@@ -103,33 +96,12 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
       int id = tid + i * kThreads;
-      int row = id / kChunks, ch = id % kChunks;
-      *reinterpret_cast<uint4*>(&sm.k[row * D + ((ch ^ (row & 7)) * 8)]) = kreg[i];
+      st_row<D>(sm.k, id / kChunks, id % kChunks, kreg[i]);
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
       int id = tid + i * kThreads;
-      if (id < kVGroups) {
-        int ch = id % kChunks, g = id / kChunks;
-        int pos = vt_pos(4 * g);  // the four keys stay adjacent: bits 0-1 unchanged
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // d = ch*8 + 2j (low halves) and d + 1 (high halves)
-          uint2 lo, hi;
-          lo.x = (w0[j] & 0xffffu) | (w1[j] << 16);
-          lo.y = (w2[j] & 0xffffu) | (w3[j] << 16);
-          hi.x = (w0[j] >> 16) | (w1[j] & 0xffff0000u);
-          hi.y = (w2[j] >> 16) | (w3[j] & 0xffff0000u);
-          int d0 = ch * 8 + 2 * j;
-          int d1 = d0 + 1;
-          *reinterpret_cast<uint2*>(&sm.vt[d0 * kBC + (((pos >> 3) ^ (d0 & 7)) * 8) + (pos & 7)]) = lo;
-          *reinterpret_cast<uint2*>(&sm.vt[d1 * kBC + (((pos >> 3) ^ (d1 & 7)) * 8) + (pos & 7)]) = hi;
-        }
-      }
+      if (id < kVGroups) st_tr4<kBC>(sm.vt, 4 * (id / kChunks), id % kChunks, vreg[i]);
     }
   }
 };
@@ -212,11 +184,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
       s[kb] = zero16();
       const int row = kb * 32 + col;
 #pragma unroll
-      for (int kk = 0; kk < kDK; ++kk) {
-        const int ch = 2 * kk + half;
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[row * D + ((ch ^ (row & 7)) * 8)]);
-        s[kb] = mfma32(a, qreg[kk], s[kb]);
-      }
+      for (int kk = 0; kk < kDK; ++kk)
+        s[kb] = mfma32(ld_row<D>(sm.k, row, 2 * kk + half), qreg[kk], s[kb]);
     }
 
     // ---- masks: keys past N, and keys after the row for causal
@@ -281,12 +250,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
         const bf16x8 b = as_bf16x8(bu);
         const int chunk = 4 * kb + 2 * m + half;
 #pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const int drow = db * 32 + col;
-          bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &sm.vt[drow * kBC + ((chunk ^ (drow & 7)) * 8)]);
-          oacc[db] = mfma32(a, b, oacc[db]);
-        }
+        for (int db = 0; db < kDB; ++db)
+          oacc[db] = mfma32(ld_tr<kBC>(sm.vt, db * 32 + col, chunk), b, oacc[db]);
       }
   }
 
