@@ -23,6 +23,8 @@ int check_common(int B, int H, int N, int d, float scale, int causal, bool* empt
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   *empty = (B == 0 || H == 0 || N == 0);
   if (*empty) return FA_OK;
+  // one head of one tensor must be addressable with 32-bit byte offsets
+  if ((long long)N * d * (long long)sizeof(float) > kMaxGrid) return FA_ERR_SHAPE;
   if (fa::forward_grid_size(B, H, N) > kMaxGrid) return FA_ERR_SHAPE;
   if (fa::backward_grid_size(B, H, N) > kMaxGrid) return FA_ERR_SHAPE;
   return FA_OK;

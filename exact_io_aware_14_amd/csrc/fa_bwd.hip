@@ -101,16 +101,13 @@ __device__ __forceinline__ void block_coords(const BwdParams& p, bool heavy_last
 }
 
 // Four consecutive rows (r0 .. r0+3 of the tile starting at `row0`) of chunk
-// `ch`, zero past N.
+// `ch`; rows past the end of the buffer read as zeros.
 template <int D>
-__device__ __forceinline__ void load_rows4(const uint16_t* base, int row0, int r0, int ch,
-                                           int N, uint4 w[4]) {
+__device__ __forceinline__ void load_rows4(__amdgpu_buffer_rsrc_t r, int row0, int r0, int ch,
+                                           uint4 w[4]) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = row0 + r0 + r;
-    const bool ok = row < N;
-    w[r] = load8<uint16_t>(base + (size_t)(ok ? row : 0) * D + ch * 8, ok);
-  }
+  for (int i = 0; i < 4; ++i)
+    w[i] = load8<uint16_t>(r, (uint32_t)((row0 + r0 + i) * D + ch * 8));
 }
 
 // ---------------------------------------------------------------- dK / dV
@@ -140,8 +137,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
   block_coords(p, false, &bh, &kblk);  // small key blocks see the most queries
   const int N = p.N;
   const size_t head = (size_t)bh * N;
-  const uint16_t* qg = p.q + head * D;
-  const uint16_t* gg = p.dout + head * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const auto qr = make_rsrc(p.q + head * D, head_bytes);
+  const auto gr = make_rsrc(p.dout + head * D, head_bytes);
 
   const int k0 = kblk * kBlock;
   const int kw0 = k0 + wave * 32;  // this wave's first key
@@ -150,12 +148,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
   // K^T and V^T columns of this lane's key, as B operands
   bf16x8 kreg[kDK], vreg[kDK];
   {
-    const bool ok = mykey < N;
-    const size_t off = (head + (ok ? mykey : 0)) * D;
+    const auto kr = make_rsrc(p.k + head * D, head_bytes);
+    const auto vr = make_rsrc(p.v + head * D, head_bytes);
 #pragma unroll
     for (int kk = 0; kk < kDK; ++kk) {
-      kreg[kk] = as_bf16x8(load8<uint16_t>(p.k + off + kk * 16 + half * 8, ok));
-      vreg[kk] = as_bf16x8(load8<uint16_t>(p.v + off + kk * 16 + half * 8, ok));
+      const uint32_t e = (uint32_t)(mykey * D + kk * 16 + half * 8);
+      kreg[kk] = as_bf16x8(load8<uint16_t>(kr, e));
+      vreg[kk] = as_bf16x8(load8<uint16_t>(vr, e));
     }
   }
   f32x16 dvacc[kDB], dkacc[kDB];
@@ -173,9 +172,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
   for (int t = t0; t < ntiles; ++t) {
     const int qs = t * kTile;
     uint4 wq[4], wg[4];
-    if (tid < kGroups) {
-      load_rows4<D>(qg, qs, 4 * sg, sch, N, wq);
-      load_rows4<D>(gg, qs, 4 * sg, sch, N, wg);
+    if (tid < kGroups) {  // wave-uniform
+      load_rows4<D>(qr, qs, 4 * sg, sch, wq);
+      load_rows4<D>(gr, qs, 4 * sg, sch, wg);
     }
     float l2 = 0.0f, dr = 0.0f;
     if (tid < kTile) {
@@ -294,8 +293,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
   block_coords(p, CAUSAL, &bh, &qblk);  // causal: late query blocks see the most keys
   const int N = p.N;
   const size_t head = (size_t)bh * N;
-  const uint16_t* kg = p.k + head * D;
-  const uint16_t* vg = p.v + head * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const auto kr = make_rsrc(p.k + head * D, head_bytes);
+  const auto vr = make_rsrc(p.v + head * D, head_bytes);
 
   const int q0 = qblk * kBlock;
   const int qw0 = q0 + wave * 32;
@@ -305,14 +305,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
   bf16x8 qreg[kDK], greg[kDK];  // Q^T and dO^T columns of this lane's row
   float l2 = INFINITY, dr = 0.0f;
   {
-    const bool ok = myq < N;
-    const size_t off = (head + (ok ? myq : 0)) * D;
+    const auto qr = make_rsrc(p.q + head * D, head_bytes);
+    const auto gr = make_rsrc(p.dout + head * D, head_bytes);
 #pragma unroll
     for (int kk = 0; kk < kDK; ++kk) {
-      qreg[kk] = as_bf16x8(load8<uint16_t>(p.q + off + kk * 16 + half * 8, ok));
-      greg[kk] = as_bf16x8(load8<uint16_t>(p.dout + off + kk * 16 + half * 8, ok));
+      const uint32_t e = (uint32_t)(myq * D + kk * 16 + half * 8);
+      qreg[kk] = as_bf16x8(load8<uint16_t>(qr, e));
+      greg[kk] = as_bf16x8(load8<uint16_t>(gr, e));
     }
-    if (ok) {
+    if (myq < N) {
       l2 = p.lse[head + myq] * kLog2e;
       dr = p.drow[head + myq];
     }
@@ -329,9 +330,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
   for (int t = 0; t < ntiles; ++t) {
     const int key0 = t * kTile;
     uint4 wk[4], wv[4];
-    if (tid < kGroups) {
-      load_rows4<D>(kg, key0, 4 * sg, sch, N, wk);
-      load_rows4<D>(vg, key0, 4 * sg, sch, N, wv);
+    if (tid < kGroups) {  // wave-uniform
+      load_rows4<D>(kr, key0, 4 * sg, sch, wk);
+      load_rows4<D>(vr, key0, 4 * sg, sch, wv);
     }
     __syncthreads();
     if (tid < kGroups) {

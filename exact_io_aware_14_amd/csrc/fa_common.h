@@ -49,30 +49,42 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
 
-// Eight consecutive elements of a row, as eight bf16 in a uint4. Storage
-// type bf16 (uint16_t) is loaded as is; fp32 is rounded to nearest even.
-// Rows past the end read as zeros.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes from `base` (raw, unstrided). Loads at
+// byte offsets at or past `bytes` return zeros, which is how rows past the
+// end of a sequence are zero-filled without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+
+// Eight consecutive elements starting at element `elem` of a buffer, as
+// eight bf16 in a uint4. Storage type bf16 (uint16_t) is loaded as is; fp32
+// is rounded to nearest even. Past the end of the buffer: zeros.
 template <typename T>
-__device__ __forceinline__ uint4 load8(const T* p, bool valid);
+__device__ __forceinline__ uint4 load8(__amdgpu_buffer_rsrc_t r, uint32_t elem);
 
 template <>
-__device__ __forceinline__ uint4 load8<uint16_t>(const uint16_t* p, bool valid) {
-  uint4 z = {0u, 0u, 0u, 0u};
-  return valid ? *reinterpret_cast<const uint4*>(p) : z;
+__device__ __forceinline__ uint4 load8<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t elem) {
+  return buf_load16(r, elem * 2u);
 }
 
 template <>
-__device__ __forceinline__ uint4 load8<float>(const float* p, bool valid) {
-  uint4 r = {0u, 0u, 0u, 0u};
-  if (valid) {
-    float4 a = reinterpret_cast<const float4*>(p)[0];
-    float4 b = reinterpret_cast<const float4*>(p)[1];
-    r.x = pack_bf16x2(a.x, a.y);
-    r.y = pack_bf16x2(a.z, a.w);
-    r.z = pack_bf16x2(b.x, b.y);
-    r.w = pack_bf16x2(b.z, b.w);
-  }
-  return r;
+__device__ __forceinline__ uint4 load8<float>(__amdgpu_buffer_rsrc_t r, uint32_t elem) {
+  const uint4 a = buf_load16(r, elem * 4u);
+  const uint4 b = buf_load16(r, elem * 4u + 16u);
+  uint4 out;
+  out.x = pack_bf16x2(__uint_as_float(a.x), __uint_as_float(a.y));
+  out.y = pack_bf16x2(__uint_as_float(a.z), __uint_as_float(a.w));
+  out.z = pack_bf16x2(__uint_as_float(b.x), __uint_as_float(b.y));
+  out.w = pack_bf16x2(__uint_as_float(b.z), __uint_as_float(b.w));
+  return out;
 }
 
 // Flip the sign of eight packed bf16 values (exact).

@@ -69,25 +69,21 @@ struct TileLoader {
   uint4 kreg[kKLoads];
   uint4 vreg[kVLoads][4];
 
-  __device__ __forceinline__ void load(const TIn* kbase, const TIn* vbase, int key0, int N,
-                                       int tid) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                       int key0, int tid) {
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
-      int id = tid + i * kThreads;
-      int row = id / kChunks, ch = id % kChunks;
-      int key = key0 + row;
-      bool ok = key < N;
-      kreg[i] = load8<TIn>(kbase + (size_t)(ok ? key : 0) * D + ch * 8, ok);
+      const int id = tid + i * kThreads;
+      kreg[i] = load8<TIn>(kr, (uint32_t)((key0 + id / kChunks) * D + (id % kChunks) * 8));
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
-      int id = tid + i * kThreads;
-      int ch = id % kChunks, g = id / kChunks;
+      const int id = tid + i * kThreads;
+      if (id < kVGroups) {  // wave-uniform
+        const int ch = id % kChunks, g = id / kChunks;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int key = key0 + 4 * g + r;
-        bool ok = (id < kVGroups) && key < N;
-        vreg[i][r] = load8<TIn>(vbase + (size_t)(ok ? key : 0) * D + ch * 8, ok);
+        for (int r = 0; r < 4; ++r)
+          vreg[i][r] = load8<TIn>(vr, (uint32_t)((key0 + 4 * g + r) * D + ch * 8));
       }
     }
   }
@@ -107,7 +103,7 @@ struct TileLoader {
 };
 
 template <int D, bool CAUSAL, typename TIn, typename TOut>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   __shared__ Smem<D> sm;
   constexpr int kDK = D / 16;  // MFMA steps along d for S^T
   constexpr int kDB = D / 32;  // 32-row blocks of O^T
@@ -136,9 +132,11 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
   const int qb = CAUSAL ? (p.nqb - 1 - qbr) : qbr;
   const int N = p.N;
   const size_t head_off = (size_t)bh * (size_t)N * D;
-  const TIn* qg = reinterpret_cast<const TIn*>(p.q) + head_off;
-  const TIn* kg = reinterpret_cast<const TIn*>(p.k) + head_off;
-  const TIn* vg = reinterpret_cast<const TIn*>(p.v) + head_off;
+  // buffer views of this head; reads past row N return zeros
+  const uint32_t head_bytes = (uint32_t)N * D * sizeof(TIn);
+  const auto qr = make_rsrc(reinterpret_cast<const TIn*>(p.q) + head_off, head_bytes);
+  const auto kr = make_rsrc(reinterpret_cast<const TIn*>(p.k) + head_off, head_bytes);
+  const auto vr = make_rsrc(reinterpret_cast<const TIn*>(p.v) + head_off, head_bytes);
 
   const int q0 = qb * kBR;                        // first row of the block
   const int qw0 = q0 + wave * kRowsPerWave;       // first row of this wave
@@ -149,8 +147,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
   bf16x8 qreg[kDK];
 #pragma unroll
   for (int kk = 0; kk < kDK; ++kk) {
-    bool ok = myq < N;
-    uint4 u = load8<TIn>(qg + (size_t)(ok ? myq : 0) * D + kk * 16 + half * 8, ok);
+    uint4 u = load8<TIn>(qr, (uint32_t)(myq * D + kk * 16 + half * 8));
     if (p.negate_q) u = negate8(u);
     qreg[kk] = as_bf16x8(u);
   }
@@ -166,13 +163,13 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
   const float c = p.c;
 
   TileLoader<D, TIn> ld;
-  ld.load(kg, vg, 0, N, tid);
+  ld.load(kr, vr, 0, tid);
 
   for (int t = 0; t < ktiles; ++t) {
     __syncthreads();  // every wave is done reading the previous tile
     ld.store(sm, tid);
     __syncthreads();
-    if (t + 1 < ktiles) ld.load(kg, vg, (t + 1) * kBC, N, tid);
+    if (t + 1 < ktiles) ld.load(kr, vr, (t + 1) * kBC, tid);
 
     const int key0 = t * kBC;
     if (CAUSAL && key0 > wave_last) continue;  // no visible key for this wave

@@ -31,8 +31,9 @@
  * - Errors: invalid arguments are reported by a nonzero status BEFORE any
  *   HIP call, and nothing is written. A launch failure returns FA_ERR_HIP.
  *   Device faults surface at the caller's next synchronisation.
- * - Sizes: B*H*N*d may exceed 2^31 elements (64-bit offsets are used);
- *   B*H*ceil(N/128) must be below 2^31.
+ * - Sizes: B*H*N*d may exceed 2^31 elements (64-bit offsets between
+ *   heads); within one head N*d*4 must be below 2^31 (N < 4194304 at
+ *   d = 128), and B*H*ceil(N/128) below 2^31. Otherwise FA_ERR_SHAPE.
  */
 #ifndef FA_H
 #define FA_H

@@ -92,6 +92,8 @@ def test_forward_validation(lib, f32):
     assert fwd(lib, N=-3, f32=f32) == FA_ERR_SHAPE
     # the grid would not fit a launch
     assert fwd(lib, B=2**20, H=2**10, N=2**16, f32=f32) == FA_ERR_SHAPE
+    # one head would not be addressable with 32-bit byte offsets
+    assert fwd(lib, N=2**22, d=128, f32=f32) == FA_ERR_SHAPE
     for i in range(5):
         args = [P] * 5
         args[i] = NULL
