@@ -1,0 +1,224 @@
+"""Throughput of exact attention, forward and forward+backward, on one MI355X.
+
+A step is one pass of the whole hot path over one batch: fa_forward, then
+fa_backward_prep and fa_backward_grads, on the causal workload B=4, H=16,
+N=4096, d=128 (bf16 inputs drawn i.i.d. N(0,1) from seed 5, already resident
+in HBM). The timed region is exactly --steps steps, bracketed by device
+synchronisation; HIP events on the launch stream also time each of the three
+launches of every step.
+
+Throughput counts matmul FLOPs only: forward 4*B*H*N^2*d, backward 2.5x that
+(score recompute, dV, dP, dQ, dK), both halved under the causal mask.
+
+Prints one JSON line. `value` is forward+backward TFLOP/s; `fwd_tflops` the
+forward alone on the same input. `roofline` describes the dominant kernel
+(the one with the longest launches), `cpu_baseline` the fp64 CPU oracle
+timed on a bounded sample of the same workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+       python bench.py --copy-calibration   (a plain 1 GiB copy, for counters)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X dense bf16 MFMA peak: 256 CUs x 4 SIMDs x 1024 flop/clk x 2.4 GHz.
+PEAK_BF16_TFLOPS = 2516.6
+WORKLOAD = "fwdbwd_causal_b4h16n4096d128"
+METRIC = "attention TFLOP/s (fwd, fwd+bwd) bf16 on 1 MI355X; % of MFMA peak"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["exact_io_aware_14_amd/csrc/fa_common.h", "exact_io_aware_14_amd/csrc/fa_fwd.hip",
+                  "exact_io_aware_14_amd/csrc/fa_bwd.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_flops(w):
+    fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    return fwd, 2.5 * fwd
+
+
+def measured_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed counter runs, if they were
+    taken on the kernel sources as they are now; else None."""
+    try:
+        data = json.load(open(PROFILE_TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    if data.get("source_hash") != src_hash:
+        return None
+    entry = data.get("kernels", {}).get(kernel)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, heads: int):
+    """The fp64 oracle on `heads` whole heads of the workload (forward and
+    backward), as TFLOP/s on the same counted-FLOP basis."""
+    import numpy as np  # noqa: F401
+
+    import oracle
+    from exact_io_aware_14_amd.inputs import draw, to_f64
+
+    q, k, v, do = draw(w.shape, w.seed, with_grad=True)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # threadpoolctl missing: numpy's BLAS default
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    for i in range(heads):
+        b, h = divmod(i, w.H)
+        qf, kf, vf, gf = (to_f64(x[b, h]) for x in (q, k, v, do))
+        oracle.forward_head(qf, kf, vf, w.scale, w.causal)
+        oracle.backward_head(qf, kf, vf, gf, w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    fwd, bwd = counted_flops(w)
+    per_head = (fwd + bwd) / (w.B * w.H)
+    return {"value": round(per_head * heads / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of {WORKLOAD}, full forward and backward "
+                      f"in fp64 numpy, {dt:.1f} s; the rate extrapolates linearly to all heads"}
+
+
+def copy_calibration():
+    """A plain device copy of 1 GiB, for scaling the FETCH_SIZE/WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=40)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit("bench.py measures one GPU only: there is no multi-GPU path here "
+                 "(attention heads would shard across GPUs with no exchange)")
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    from exact_io_aware_14_amd import (fa_backward_grads, fa_backward_prep,
+                                       fa_backward_workspace_size, fa_forward)
+    from exact_io_aware_14_amd.inputs import by_name, draw
+
+    w = by_name(WORKLOAD)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x.to(dev) for x in draw(w.shape, w.seed, with_grad=True))
+    o = torch.empty_like(q)
+    lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa_backward_workspace_size(*w.shape), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa_forward(q, k, v, w.scale, w.causal, o, lse, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa_backward_prep(o, do, ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fa_backward_grads(q, k, v, do, lse, ws, w.scale, w.causal, dq, dk, dv, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    prep_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    grads_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    fwd_f, bwd_f = counted_flops(w)
+    value = (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
+    fwd_tflops = fwd_f / (fwd_ms * 1e-3) / 1e12
+    bwd_tflops = bwd_f / ((prep_ms + grads_ms) * 1e-3) / 1e12
+
+    src_hash = kernel_source_hash()
+    if grads_ms >= fwd_ms:
+        kname, kflops, kms = "bwd_grads_kernel<128,causal>", bwd_f, grads_ms
+    else:
+        kname, kflops, kms = "fwd_kernel<128,causal>", fwd_f, fwd_ms
+    achieved = kflops / (kms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(kname, src_hash),
+                "avg_launch_ms": round(kms, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "seed": w.seed, "scale": w.scale},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "bwd_tflops": round(bwd_tflops, 2),
+        "ms": {"fwd": round(fwd_ms, 4), "bwd_prep": round(prep_ms, 4),
+               "bwd_grads": round(grads_ms, 4)},
+        "wall_s_timed": round(wall, 3),
+        "kernel_source_hash": src_hash,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

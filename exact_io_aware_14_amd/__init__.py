@@ -13,8 +13,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["FAError", "fa_forward", "fa_forward_f32", "fa_backward",
-           "fa_backward_workspace_size", "fa_strerror", "library", "LIB_PATH"]
+__all__ = ["FAError", "fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_prep",
+           "fa_backward_grads", "fa_backward_workspace_size", "fa_strerror", "library",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -45,6 +46,11 @@ def library():
         lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
                                     vp, sz, vp]
         lib.fa_backward.restype = i
+        lib.fa_backward_prep.argtypes = [vp, vp, i, i, i, i, vp, sz, vp]
+        lib.fa_backward_prep.restype = i
+        lib.fa_backward_grads.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
+                                          vp, sz, vp]
+        lib.fa_backward_grads.restype = i
         lib.fa_strerror.argtypes = [i]
         lib.fa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -122,34 +128,75 @@ def fa_forward_f32(q, k, v, scale=None, causal=False, o=None, lse=None, stream=N
                     _torch().float32)
 
 
-def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
-                workspace=None, stream=None):
-    """dQ, dK, dV of sum(dout * O) (see fa_backward in fa.h)."""
+def _bwd_check(q, tensors, lse, outs):
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
     dev = q.device
-    bf = torch.bfloat16
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        _check(t, name, bf, (B, H, N, d), dev)
-    _check(lse, "lse", torch.float32, (B, H, N), dev)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check(t, name, bf, (B, H, N, d), dev)
-    need = fa_backward_workspace_size(B, H, N, d)
+    for name, t in tensors:
+        _check(t, name, torch.bfloat16, (B, H, N, d), dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, N), dev)
+    res = []
+    for name, t in outs:
+        t = torch.empty_like(q) if t is None else t
+        _check(t, name, torch.bfloat16, (B, H, N, d), dev)
+        res.append(t)
+    return (B, H, N, d), dev, res
+
+
+def _workspace(shape, dev, workspace):
+    torch = _torch()
+    need = fa_backward_workspace_size(*shape)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     if workspace.device != dev:
         raise ValueError("workspace must be on the same device")
-    if scale is None:
-        scale = d ** -0.5
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
+                workspace=None, stream=None):
+    """dQ, dK, dV of sum(dout * O) (see fa_backward in fa.h)."""
+    shape, dev, (dq, dk, dv) = _bwd_check(
+        q, (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)), lse,
+        (("dq", dq), ("dk", dk), ("dv", dv)))
+    ws, ws_bytes = _workspace(shape, dev, workspace)
+    scale = shape[3] ** -0.5 if scale is None else scale
     st = library().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
-                               int(bool(causal)), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream))
+                               _ptr(dq), _ptr(dk), _ptr(dv), *shape, float(scale),
+                               int(bool(causal)), _ptr(ws), ws_bytes, _stream(stream))
     if st != 0:
         raise FAError(st, "fa_backward")
+    return dq, dk, dv
+
+
+def fa_backward_prep(o, dout, workspace=None, stream=None):
+    """Row terms D_i = sum_k dout_ik O_ik into the workspace (see fa.h); returns it."""
+    shape, dev, _ = _bwd_check(o, (("o", o), ("dout", dout)), None, ())
+    ws, ws_bytes = _workspace(shape, dev, workspace)
+    st = library().fa_backward_prep(_ptr(o), _ptr(dout), *shape, _ptr(ws), ws_bytes,
+                                    _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_backward_prep")
+    return ws
+
+
+def fa_backward_grads(q, k, v, dout, lse, workspace, scale=None, causal=False, dq=None,
+                      dk=None, dv=None, stream=None):
+    """dQ, dK, dV from the row terms fa_backward_prep left in `workspace` (see fa.h)."""
+    shape, dev, (dq, dk, dv) = _bwd_check(
+        q, (("q", q), ("k", k), ("v", v), ("dout", dout)), lse,
+        (("dq", dq), ("dk", dk), ("dv", dv)))
+    if workspace is None or workspace.device != dev:
+        raise ValueError("workspace from fa_backward_prep is required, on the same device")
+    scale = shape[3] ** -0.5 if scale is None else scale
+    st = library().fa_backward_grads(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), *shape, float(scale),
+                                     int(bool(causal)), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_backward_grads")
     return dq, dk, dv

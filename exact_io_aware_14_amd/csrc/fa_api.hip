@@ -38,6 +38,10 @@ int check_ptrs(const void* const* ptrs, int n) {
   return FA_OK;
 }
 
+bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d) {
+  return ws != nullptr && aligned16(ws) && bytes >= fa_backward_workspace_size(B, H, N, d);
+}
+
 int forward_common(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int H, int N, int d, float scale, int causal, hipStream_t stream,
                    bool f32) {
@@ -71,6 +75,37 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
+int fa_backward_prep(const void* o, const void* dout, int B, int H, int N, int d,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, 1.0f, 0, &empty);
+  if (st != FA_OK || empty) return st;
+  const void* ptrs[2] = {o, dout};
+  st = check_ptrs(ptrs, 2);
+  if (st != FA_OK) return st;
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
+  fa::BwdArgs a{nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr,
+                static_cast<float*>(workspace), B, H, N, d, 1.0f, 0, stream};
+  return fa::launch_backward_prep(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_backward_grads(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int N,
+                      int d, float scale, int causal, const void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  const void* ptrs[8] = {q, k, v, dout, lse, dq, dk, dv};
+  st = check_ptrs(ptrs, 8);
+  if (st != FA_OK) return st;
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
+  fa::BwdArgs a{q, k, v, nullptr, dout, lse, dq, dk, dv,
+                static_cast<float*>(const_cast<void*>(workspace)), B, H, N, d, scale, causal,
+                stream};
+  return fa::launch_backward_grads(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                 float scale, int causal, void* workspace, size_t workspace_bytes,
@@ -81,13 +116,11 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
   const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
   st = check_ptrs(ptrs, 9);
   if (st != FA_OK) return st;
-  if (workspace == nullptr || !aligned16(workspace) ||
-      workspace_bytes < fa_backward_workspace_size(B, H, N, d))
-    return FA_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace),
                 B, H, N, d, scale, causal, stream};
-  hipError_t e = fa::launch_backward(a);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  if (fa::launch_backward_prep(a) != hipSuccess) return FA_ERR_HIP;
+  return fa::launch_backward_grads(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_strerror(int status) {

@@ -1,11 +1,13 @@
-// Backward exact attention for gfx950, in three launches on one stream:
+// Backward exact attention for gfx950, in two launches on one stream:
 //
-//   1. rows:  D_i = sum_k dO_ik O_ik                            (HBM-bound)
-//   2. dK/dV: one workgroup per (batch, head, block of 128 keys); it walks
-//             the query tiles and accumulates dV_j = sum_i P_ij dO_i and
-//             dK_j = scale * sum_i dS_ij Q_i for its own keys
-//   3. dQ:    one workgroup per (batch, head, block of 128 query rows); it
-//             walks the key tiles and accumulates dQ_i = scale * sum_j dS_ij K_j
+//   prep:  D_i = sum_k dO_ik O_ik                               (HBM-bound)
+//   grads: one launch holding two kinds of workgroup, interleaved so the
+//          most expensive ones of both kinds start first:
+//          dK/dV jobs, one per (batch, head, block of 128 keys), walk the
+//          query tiles and accumulate dV_j = sum_i P_ij dO_i and
+//          dK_j = scale * sum_i dS_ij Q_i for their own keys;
+//          dQ jobs, one per (batch, head, block of 128 query rows), walk the
+//          key tiles and accumulate dQ_i = scale * sum_j dS_ij K_j
 //
 // with P_ij = exp(scale q_i.k_j - lse_i) recomputed from the forward pass's
 // logsumexp instead of being stored ("Flash Attention: بهینه‌سازی مکانیزم
@@ -83,21 +85,36 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(const uint16_t* o,
   if (ch == 0 && row < rows) drow[row] = acc;
 }
 
-// (head, block) of this workgroup; `heavy_last` puts the largest block
-// indices first (the rows that see the most keys under a causal mask).
-__device__ __forceinline__ void block_coords(const BwdParams& p, bool heavy_last, int* bh,
-                                             int* blk) {
+// Job of this workgroup in the grads launch. Every head owns 2*nblk jobs,
+// alternately dK/dV and dQ, each sequence ordered from the most expensive
+// block down (causal: dK/dV of the first key blocks, dQ of the last query
+// blocks). Consecutive workgroups go to the 8 XCDs in turn; when the head
+// count allows, each XCD gets whole heads so their K/V and Q/dO stay in its L2.
+struct Job {
+  int bh;
+  int blk;
+  bool is_dq;
+};
+
+template <bool CAUSAL>
+__device__ __forceinline__ Job job_of(const BwdParams& p) {
   const int L = blockIdx.x;
-  int rank;
+  const int per_head = 2 * p.nblk;
+  int bh, j;
   if (p.xcd_remap) {
     const int xcd = L & 7, idx = L >> 3;
-    *bh = (idx / p.nblk) * 8 + xcd;
-    rank = idx % p.nblk;
+    bh = (idx / per_head) * 8 + xcd;
+    j = idx % per_head;
   } else {
-    *bh = L % p.BH;
-    rank = L / p.BH;
+    bh = L % p.BH;
+    j = L / p.BH;
   }
-  *blk = heavy_last ? (p.nblk - 1 - rank) : rank;
+  Job job;
+  job.bh = bh;
+  job.is_dq = (j & 1) != 0;
+  const int rank = j >> 1;
+  job.blk = (CAUSAL && job.is_dq) ? (p.nblk - 1 - rank) : rank;
+  return job;
 }
 
 // Four consecutive rows (r0 .. r0+3 of the tile starting at `row0`) of chunk
@@ -122,9 +139,19 @@ struct KVSmem {
   float dr[kTile];          // D_i; 0 past N
 };
 
+template <int D>
+struct QSmem {
+  uint16_t k[kTile * D];   // K tile, row-major
+  uint16_t kt[D * kTile];  // K tile, transposed
+  uint16_t v[kTile * D];   // V tile, row-major
+};
+
+template <int D>
+constexpr size_t kGradsSmem = sizeof(KVSmem<D>) > sizeof(QSmem<D>) ? sizeof(KVSmem<D>)
+                                                                     : sizeof(QSmem<D>);
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
-  __shared__ KVSmem<D> sm;
+__device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk, KVSmem<D>& sm) {
   constexpr int kDK = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kChunks = D / 8;
@@ -133,8 +160,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  int bh, kblk;
-  block_coords(p, false, &bh, &kblk);  // small key blocks see the most queries
   const int N = p.N;
   const size_t head = (size_t)bh * N;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -169,19 +194,25 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
   const float c = p.c;
   const int sg = tid / kChunks, sch = tid % kChunks;  // staging group of this thread
 
-  for (int t = t0; t < ntiles; ++t) {
+  // registers holding the next tile while the current one is computed
+  uint4 wq[4], wg[4];
+  float l2 = 0.0f, dr = 0.0f;
+  auto fetch = [&](int t) {
     const int qs = t * kTile;
-    uint4 wq[4], wg[4];
     if (tid < kGroups) {  // wave-uniform
       load_rows4<D>(qr, qs, 4 * sg, sch, wq);
       load_rows4<D>(gr, qs, 4 * sg, sch, wg);
     }
-    float l2 = 0.0f, dr = 0.0f;
     if (tid < kTile) {
       const int row = qs + tid;
       l2 = row < N ? p.lse[head + row] * kLog2e : INFINITY;
       dr = row < N ? p.drow[head + row] : 0.0f;
     }
+  };
+  if (t0 < ntiles) fetch(t0);
+
+  for (int t = t0; t < ntiles; ++t) {
+    const int qs = t * kTile;
     __syncthreads();  // the previous tile is no longer read
     if (tid < kGroups) {
 #pragma unroll
@@ -197,6 +228,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
       sm.dr[tid] = dr;
     }
     __syncthreads();
+    if (t + 1 < ntiles) fetch(t + 1);
 
     if (CAUSAL && qs + kTile - 1 < kw0) continue;  // every row of the tile precedes our keys
     const bool need_mask = CAUSAL && qs < kw0 + 31;
@@ -271,16 +303,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dQ
 
-template <int D>
-struct QSmem {
-  uint16_t k[kTile * D];   // K tile, row-major
-  uint16_t kt[D * kTile];  // K tile, transposed
-  uint16_t v[kTile * D];   // V tile, row-major
-};
-
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
-  __shared__ QSmem<D> sm;
+__device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk, QSmem<D>& sm) {
   constexpr int kDK = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kChunks = D / 8;
@@ -289,8 +313,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  int bh, qblk;
-  block_coords(p, CAUSAL, &bh, &qblk);  // causal: late query blocks see the most keys
   const int N = p.N;
   const size_t head = (size_t)bh * N;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -327,13 +349,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
   const float c = p.c;
   const int sg = tid / kChunks, sch = tid % kChunks;
 
+  uint4 wk[4], wv[4];
+  auto fetch = [&](int t) {
+    if (tid < kGroups) {  // wave-uniform
+      load_rows4<D>(kr, t * kTile, 4 * sg, sch, wk);
+      load_rows4<D>(vr, t * kTile, 4 * sg, sch, wv);
+    }
+  };
+  fetch(0);
+
   for (int t = 0; t < ntiles; ++t) {
     const int key0 = t * kTile;
-    uint4 wk[4], wv[4];
-    if (tid < kGroups) {  // wave-uniform
-      load_rows4<D>(kr, key0, 4 * sg, sch, wk);
-      load_rows4<D>(vr, key0, 4 * sg, sch, wv);
-    }
     __syncthreads();
     if (tid < kGroups) {
 #pragma unroll
@@ -344,6 +370,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
       st_tr4<kTile>(sm.kt, 4 * sg, sch, wk);
     }
     __syncthreads();
+    if (t + 1 < ntiles) fetch(t + 1);
 
     if (CAUSAL && key0 > wave_last) continue;
     const bool need_mask = (key0 + kTile > N) || (CAUSAL && key0 + kTile - 1 > qw0);
@@ -402,7 +429,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_typed(const BwdArgs& a) {
+__global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kGradsSmem<D>];
+  const Job job = job_of<CAUSAL>(p);
+  if (job.is_dq)
+    dq_job<D, CAUSAL>(p, job.bh, job.blk, *reinterpret_cast<QSmem<D>*>(smem));
+  else
+    dkdv_job<D, CAUSAL>(p, job.bh, job.blk, *reinterpret_cast<KVSmem<D>*>(smem));
+}
+
+template <int D>
+BwdParams make_params(const BwdArgs& a) {
   BwdParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -419,33 +456,44 @@ hipError_t launch_typed(const BwdArgs& a) {
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
   p.xcd_remap = (p.BH % 8) == 0;
+  return p;
+}
 
-  const long long rows = (long long)p.BH * p.N;
+template <int D>
+hipError_t launch_prep_typed(const BwdArgs& a) {
+  const long long rows = (long long)a.B * a.H * a.N;
   constexpr int kRowsPerBlock = kThreads / (D / 8);
-  const dim3 rgrid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  hipLaunchKernelGGL((bwd_rows_kernel<D>), rgrid, dim3(kThreads), 0, a.stream,
-                     static_cast<const uint16_t*>(a.o), p.dout, a.drow, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((long long)p.BH * p.nblk));
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, a.stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, a.stream, p);
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((bwd_rows_kernel<D>), grid, dim3(kThreads), 0, a.stream,
+                     static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
+                     a.drow, rows);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_grads_typed(const BwdArgs& a) {
+  const BwdParams p = make_params<D>(a);
+  const dim3 grid((unsigned)(2LL * p.BH * p.nblk));
+  hipLaunchKernelGGL((bwd_grads_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_backward(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_typed<64, true>(a) : launch_typed<64, false>(a);
-  return a.causal ? launch_typed<128, true>(a) : launch_typed<128, false>(a);
+hipError_t launch_backward_prep(const BwdArgs& a) {
+  return a.d == 64 ? launch_prep_typed<64>(a) : launch_prep_typed<128>(a);
+}
+
+hipError_t launch_backward_grads(const BwdArgs& a) {
+  if (a.d == 64)
+    return a.causal ? launch_grads_typed<64, true>(a) : launch_grads_typed<64, false>(a);
+  return a.causal ? launch_grads_typed<128, true>(a) : launch_grads_typed<128, false>(a);
 }
 
 long long backward_grid_size(int B, int H, int N) {
   const long long rows = (long long)B * H * N;
   const long long row_blocks = (rows + 15) / 16;
-  const long long blocks = (long long)B * H * ((N + kBlock - 1) / kBlock);
+  const long long blocks = 2LL * B * H * ((N + kBlock - 1) / kBlock);
   return row_blocks > blocks ? row_blocks : blocks;
 }
 

@@ -112,7 +112,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // * transposed [d][pos(row)]: each LDS row holds one column d of the tile.
 //   Rows are stored at position pos(r), r with bits 2 and 3 swapped, which
 //   makes the eight rows one lane needs for one MFMA operand (see below)
-//   contiguous; chunks are swizzled by d & 7 in the same way.
+//   contiguous. Chunks are XOR-swizzled by (d ^ d/8) & 7: the 32 lanes of a
+//   read cover 32 consecutive columns d (distinct d & 7 within every 8
+//   lanes), while the 16 lanes of a transposing store cover columns 8 apart
+//   (distinct d/8), so neither direction piles onto one bank.
 //
 // Why the swap: an accumulator element r of the 32x32 MFMA covers row
 // 8*(r/4) + 4h + (r%4) of its 32-row block. Repacking accumulator elements
@@ -124,6 +127,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ int tpos(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
+
+// Chunk swizzle of column d of a transposed tile.
+__device__ __forceinline__ int tsw(int d) { return (d ^ (d >> 3)) & 7; }
 
 // Store chunk `ch` (8 elements) of row `row` into a row-major tile of width D.
 template <int D>
@@ -154,8 +160,8 @@ __device__ __forceinline__ void st_tr4(uint16_t* tile, int r0, int ch, const uin
     hi.x = (w0[j] >> 16) | (w1[j] & 0xffff0000u);
     hi.y = (w2[j] >> 16) | (w3[j] & 0xffff0000u);
     const int d0 = ch * 8 + 2 * j, d1 = d0 + 1;
-    *reinterpret_cast<uint2*>(&tile[d0 * R + (((pos >> 3) ^ (d0 & 7)) * 8) + (pos & 7)]) = lo;
-    *reinterpret_cast<uint2*>(&tile[d1 * R + (((pos >> 3) ^ (d1 & 7)) * 8) + (pos & 7)]) = hi;
+    *reinterpret_cast<uint2*>(&tile[d0 * R + (((pos >> 3) ^ tsw(d0)) * 8) + (pos & 7)]) = lo;
+    *reinterpret_cast<uint2*>(&tile[d1 * R + (((pos >> 3) ^ tsw(d1)) * 8) + (pos & 7)]) = hi;
   }
 }
 
@@ -163,7 +169,7 @@ __device__ __forceinline__ void st_tr4(uint16_t* tile, int r0, int ch, const uin
 // 8*chunk .. 8*chunk+7.
 template <int R>
 __device__ __forceinline__ bf16x8 ld_tr(const uint16_t* tile, int d, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(&tile[d * R + ((chunk ^ (d & 7)) * 8)]);
+  return *reinterpret_cast<const bf16x8*>(&tile[d * R + ((chunk ^ tsw(d)) * 8)]);
 }
 
 }  // namespace fa

@@ -47,7 +47,7 @@ struct FwdParams {
   int BH;        // batch * heads
   int N;         // sequence length
   int nqb;       // query blocks per head
-  float c;       // |scale| * log2(e)
+  float c;       // |scale| * log2(e), at least 1e-30
   int negate_q;  // scale < 0: Q is negated on load and |scale| is used
   int xcd_remap; // heads grouped per XCD (requires BH % 8 == 0)
 };
@@ -205,13 +205,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, swap_halves(mx));
-    const float cand = (mx == -INFINITY) ? -INFINITY : mx * c;
+    // c > 0, so a fully masked row gives cand = -inf and never grows m_run
+    const float cand = mx * c;
 
-    // ---- move the reference maximum only when it is exceeded by the slack
+    // ---- move the reference maximum only when it is exceeded by the slack.
+    // Every row sees key 0 in the first tile, so m_run is finite from then on
+    // (on the first tile alpha = 2^-inf = 0 clears the empty accumulators).
     const bool grow = cand > m_run + kRescaleSlack;
     if (__any(grow)) {
       const float m_new = fmaxf(m_run, cand);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+      const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < kDB; ++i)
@@ -219,24 +222,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
       m_run = m_new;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
 
-    // ---- probabilities p = 2^(c*s - m), summed and packed to bf16
+    // ---- probabilities p = 2^(c*s - m) (masked scores: 2^-inf = 0), summed
+    // in fp32 (lse keeps fp32 accuracy) and packed to bf16 for P.V
     uint32_t pk[kKB][8];
-    float lsum = 0.0f;
+    float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
-      float e[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-        if (need_mask) e[r] = (s[kb][r] == -INFINITY) ? 0.0f : e[r];
-        lsum += e[r];
+      for (int r = 0; r < 8; ++r) {
+        const float e0 = fast_exp2(__builtin_fmaf(s[kb][2 * r], c, -m_run));
+        const float e1 = fast_exp2(__builtin_fmaf(s[kb][2 * r + 1], c, -m_run));
+        ls0 += e0;
+        ls1 += e1;
+        pk[kb][r] = pack_bf16x2(e0, e1);
       }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) pk[kb][r] = pack_bf16x2(e[2 * r], e[2 * r + 1]);
     }
-    l_run += lsum;
+    l_run += ls0 + ls1;
 
     // ---- O^T += V^T P^T; P^T slots (kb, m) are accumulator rows 8m..8m+7
 #pragma unroll
@@ -289,7 +291,9 @@ hipError_t launch_typed(const FwdArgs& a) {
   p.BH = a.B * a.H;
   p.N = a.N;
   p.nqb = (a.N + kBR - 1) / kBR;
-  p.c = fabsf(a.scale) * kLog2e;
+  // c is kept positive: a zero or denormal scale is raised to 1e-30, which
+  // changes no score by more than 1e-27 and keeps c * (-inf) = -inf
+  p.c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   p.negate_q = a.scale < 0.0f;
   p.xcd_remap = (p.BH % 8) == 0;
   dim3 grid((unsigned)((long long)p.BH * p.nqb));

@@ -38,7 +38,8 @@ struct BwdArgs {
 
 hipError_t launch_forward_bf16(const FwdArgs& a);
 hipError_t launch_forward_f32(const FwdArgs& a);
-hipError_t launch_backward(const BwdArgs& a);
+hipError_t launch_backward_prep(const BwdArgs& a);   // uses o, dout, drow
+hipError_t launch_backward_grads(const BwdArgs& a);  // uses everything but o
 
 // Workgroups the forward launch uses (for grid-size validation).
 long long forward_grid_size(int B, int H, int N);

@@ -90,7 +90,10 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d);
 /*
  * Backward pass: gradients of sum(dout * O) with respect to q, k and v,
  * O = softmax(scale Q K^T) V. The probabilities are recomputed from lse; no
- * N x N matrix is stored (deepfa.ir page, recomputation technique).
+ * N x N matrix is stored (deepfa.ir page, recomputation technique). The
+ * pages print no backward equations; the ones used are the derivative of
+ * the forward definition: with P the softmax, D_i = sum_k dout_ik O_ik,
+ * dS = P * (dout V^T - D), dq = scale dS K, dk = scale dS^T Q, dv = P^T dout.
  *   q, k, v, o, dout : [B,H,N,d] bf16 inputs; o and lse are the outputs of
  *                      fa_forward on the same q, k, v, scale and causal.
  *   lse              : [B,H,N] fp32 input.
@@ -98,14 +101,34 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d);
  *                      fp32 accumulation, rounded to nearest even once.
  *   workspace        : device buffer of at least
  *                      fa_backward_workspace_size(B,H,N,d) bytes, 16-byte
- *                      aligned, contents ignored on entry and clobbered.
- * dq is accumulated without atomics: one pass over K/V column blocks writes
- * dk and dv, a second pass over Q row blocks writes dq.
+ *                      aligned; contents ignored on entry, holds D on return.
+ * Equivalent to fa_backward_prep followed by fa_backward_grads on the same
+ * stream. Every output element is written by exactly one workgroup: dk and
+ * dv by a pass over key blocks, dq by a pass over query-row blocks, with no
+ * atomics, so results are bitwise reproducible.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, int causal,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * First stage of fa_backward: D_i = sum_k dout_ik O_ik for every row, into
+ * the workspace ([B,H,N] fp32). o and dout as for fa_backward. Errors as for
+ * fa_backward (scale and causal are not arguments here).
+ */
+int fa_backward_prep(const void* o, const void* dout, int B, int H, int N, int d,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Second stage of fa_backward: dq, dk, dv from q, k, v, dout, lse and the
+ * row terms D that fa_backward_prep left in `workspace` (read only here).
+ * Arguments, layouts and errors as for fa_backward.
+ */
+int fa_backward_grads(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, float scale, int causal,
+                      const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);

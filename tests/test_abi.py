@@ -37,8 +37,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_workspace_size",
-            "fa_strerror"} <= set(names)
+    assert {"fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_prep",
+            "fa_backward_grads", "fa_backward_workspace_size", "fa_strerror"} <= set(names)
     raw = ctypes.CDLL(fa.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), f"{name} declared in include/ but not exported"
@@ -121,6 +121,34 @@ def test_backward_validation(lib):
     assert bwd(lib, ws=PM) == FA_ERR_WORKSPACE
     assert bwd(lib, ws_bytes=16 * 4 - 1) == FA_ERR_WORKSPACE
     assert bwd(lib, ptrs=[NULL] * 9, ws=NULL, N=0) == FA_OK
+
+
+def test_backward_stage_validation(lib):
+    ws = 16 * 4
+    assert lib.fa_backward_prep(P, P, 1, 1, 16, 80, P, ws, NULL) == FA_ERR_HEADDIM
+    assert lib.fa_backward_prep(P, P, 1, -1, 16, 64, P, ws, NULL) == FA_ERR_SHAPE
+    assert lib.fa_backward_prep(NULL, P, 1, 1, 16, 64, P, ws, NULL) == FA_ERR_NULL
+    assert lib.fa_backward_prep(P, PM, 1, 1, 16, 64, P, ws, NULL) == FA_ERR_ALIGN
+    assert lib.fa_backward_prep(P, P, 1, 1, 16, 64, P, ws - 4, NULL) == FA_ERR_WORKSPACE
+    assert lib.fa_backward_prep(P, P, 1, 1, 16, 64, NULL, ws, NULL) == FA_ERR_WORKSPACE
+    assert lib.fa_backward_prep(NULL, NULL, 1, 1, 0, 64, NULL, 0, NULL) == FA_OK
+
+    def grads(ptrs=None, d=64, N=16, causal=0, scale=0.125, w=P, wb=ws):
+        ptrs = ptrs or [P] * 8
+        return lib.fa_backward_grads(*ptrs, 1, 1, N, d, scale, causal, w, wb, NULL)
+    assert grads(causal=5) == FA_ERR_ARG
+    assert grads(scale=float("nan")) == FA_ERR_ARG
+    assert grads(d=32) == FA_ERR_HEADDIM
+    assert grads(N=-4) == FA_ERR_SHAPE
+    for i in range(8):
+        ptrs = [P] * 8
+        ptrs[i] = NULL
+        assert grads(ptrs=ptrs) == FA_ERR_NULL
+        ptrs[i] = PM
+        assert grads(ptrs=ptrs) == FA_ERR_ALIGN
+    assert grads(w=NULL) == FA_ERR_WORKSPACE
+    assert grads(wb=ws - 1) == FA_ERR_WORKSPACE
+    assert grads(ptrs=[NULL] * 8, N=0, w=NULL, wb=0) == FA_OK
 
 
 def test_python_binding_without_gpu_raises_cleanly(lib):

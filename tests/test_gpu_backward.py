@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import oracle
-from exact_io_aware_14_amd import fa_backward, fa_backward_workspace_size, fa_forward
+from exact_io_aware_14_amd import (fa_backward, fa_backward_grads, fa_backward_prep,
+                                   fa_backward_workspace_size, fa_forward)
 from exact_io_aware_14_amd.inputs import WORKLOADS, draw, to_f64
 from parity import check_grad, check_o, log, sample_heads
 
@@ -103,6 +104,23 @@ def test_backward_writes_every_output_and_is_deterministic():
         results.append([g.clone() for g in grads])
     for a, b in zip(results[0], results[1]):
         assert torch.equal(a, b)
+
+
+def test_backward_stages_match_backward():
+    """fa_backward_prep + fa_backward_grads give bitwise the result of fa_backward."""
+    for shape, causal in (((2, 2, 333, 128), True), ((1, 3, 200, 64), False)):
+        q, k, v, do = (x.to(DEV) for x in draw(shape, 44, with_grad=True))
+        o, lse = fa_forward(q, k, v, causal=causal)
+        ref = fa_backward(q, k, v, o, do, lse, causal=causal)
+        ws = fa_backward_prep(o, do)
+        # the row terms are D_i = sum_k dO_ik O_ik
+        drow = ws[: shape[0] * shape[1] * shape[2] * 4].view(torch.float32).view(shape[:3])
+        expect = (do.float() * o.float()).sum(-1)
+        assert torch.allclose(drow, expect, rtol=1e-5, atol=1e-5)
+        got = fa_backward_grads(q, k, v, do, lse, ws, causal=causal)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b)
 
 
 def test_backward_empty_is_noop():
