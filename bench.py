@@ -145,7 +145,7 @@ def main():
         fa_forward(q, k, v, w.scale, w.causal, o, lse, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        fa_backward_prep(o, do, ws, stream=stream)
+        fa_backward_prep(o, do, lse, ws, stream=stream)
         if ev is not None:
             ev[2].record(stream)
         fa_backward_grads(q, k, v, do, lse, ws, w.scale, w.causal, dq, dk, dv, stream=stream)

@@ -46,7 +46,7 @@ def library():
         lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
                                     vp, sz, vp]
         lib.fa_backward.restype = i
-        lib.fa_backward_prep.argtypes = [vp, vp, i, i, i, i, vp, sz, vp]
+        lib.fa_backward_prep.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
         lib.fa_backward_prep.restype = i
         lib.fa_backward_grads.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
                                           vp, sz, vp]
@@ -172,11 +172,11 @@ def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=Non
     return dq, dk, dv
 
 
-def fa_backward_prep(o, dout, workspace=None, stream=None):
-    """Row terms D_i = sum_k dout_ik O_ik into the workspace (see fa.h); returns it."""
-    shape, dev, _ = _bwd_check(o, (("o", o), ("dout", dout)), None, ())
+def fa_backward_prep(o, dout, lse, workspace=None, stream=None):
+    """Row terms (D_i = sum_k dout_ik O_ik, lse_i log2 e) into the workspace (see fa.h)."""
+    shape, dev, _ = _bwd_check(o, (("o", o), ("dout", dout)), lse, ())
     ws, ws_bytes = _workspace(shape, dev, workspace)
-    st = library().fa_backward_prep(_ptr(o), _ptr(dout), *shape, _ptr(ws), ws_bytes,
+    st = library().fa_backward_prep(_ptr(o), _ptr(dout), _ptr(lse), *shape, _ptr(ws), ws_bytes,
                                     _stream(stream))
     if st != 0:
         raise FAError(st, "fa_backward_prep")

@@ -72,19 +72,19 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
-  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  return 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);  // D and lse * log2(e)
 }
 
-int fa_backward_prep(const void* o, const void* dout, int B, int H, int N, int d,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int fa_backward_prep(const void* o, const void* dout, const float* lse, int B, int H, int N,
+                     int d, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   bool empty = false;
   int st = check_common(B, H, N, d, 1.0f, 0, &empty);
   if (st != FA_OK || empty) return st;
-  const void* ptrs[2] = {o, dout};
-  st = check_ptrs(ptrs, 2);
+  const void* ptrs[3] = {o, dout, lse};
+  st = check_ptrs(ptrs, 3);
   if (st != FA_OK) return st;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
-  fa::BwdArgs a{nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr,
+  fa::BwdArgs a{nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr, nullptr,
                 static_cast<float*>(workspace), B, H, N, d, 1.0f, 0, stream};
   return fa::launch_backward_prep(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -1,6 +1,7 @@
 // Backward exact attention for gfx950, in two launches on one stream:
 //
-//   prep:  D_i = sum_k dO_ik O_ik                               (HBM-bound)
+//   prep:  D_i = sum_k dO_ik O_ik and lse2_i = lse_i * log2(e) for every row
+//          (HBM-bound), into the workspace
 //   grads: one launch holding two kinds of workgroup, interleaved so the
 //          most expensive ones of both kinds start first:
 //          dK/dV jobs, one per (batch, head, block of 128 keys), walk the
@@ -21,12 +22,18 @@
 // workgroup, so no atomics are needed and results are deterministic.
 //
 // MFMA formulations (32x32x16 bf16; layouts in fa_common.h):
-//   dK/dV kernel, lane = key:   S = Q K^T and dP = dO V^T with K^T, V^T held
-//     in registers as B operands; dV^T += dO^T P and dK^T += Q^T dS with the
-//     probabilities repacked in-lane as B operands and dO^T, Q^T transposed
-//     in LDS as A operands.
-//   dQ kernel, lane = query:    S^T = K Q^T and dP^T = V dO^T with Q^T, dO^T
-//     in registers; dQ^T += K^T dS^T with K^T transposed in LDS.
+//   dK/dV job, lane = key:   S = Q K^T and dP = dO V^T with K^T, V^T held in
+//     registers as B operands and Q, dO rows read from LDS; dV^T += dO^T P
+//     and dK^T += Q^T dS with P, dS repacked in-lane as B operands and dO^T,
+//     Q^T read from the same row-major tiles through the transposing read.
+//   dQ job, lane = query:    S^T = K Q^T and dP^T = V dO^T with Q^T, dO^T in
+//     registers; dQ^T += K^T dS^T with K^T read through the transposing read.
+//
+// Tiles of 64 rows move global -> LDS with direct buffer loads (no
+// registers), double-buffered: tile t+1 loads while tile t is computed, one
+// barrier per tile. Rows past the end of a sequence load as zeros, so they
+// add nothing to any gradient (their Q, dO, K and V are zero); only the
+// causal mask needs explicit handling, on diagonal tiles.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -34,6 +41,7 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
 constexpr int kBlock = 128;  // keys (dK/dV) or query rows (dQ) per workgroup
 constexpr int kTile = 64;    // rows of the streamed tile
 
@@ -42,8 +50,8 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* lse;
-  const float* drow;
+  const float* drow;  // D_i
+  const float* lse2;  // lse_i * log2(e)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -58,12 +66,13 @@ struct BwdParams {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// ---------------------------------------------------------------- rows
+// ---------------------------------------------------------------- prep
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_rows_kernel(const uint16_t* o,
-                                                            const uint16_t* dout, float* drow,
-                                                            long long rows) {
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t* o,
+                                                            const uint16_t* dout,
+                                                            const float* lse, float* drow,
+                                                            float* lse2, long long rows) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerBlock = kThreads / kLanesPerRow;
   const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
@@ -82,8 +91,13 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(const uint16_t* o,
   }
 #pragma unroll
   for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (ch == 0 && row < rows) drow[row] = acc;
+  if (ch == 0 && row < rows) {
+    drow[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
+
+// ---------------------------------------------------------------- layout
 
 // Job of this workgroup in the grads launch. Every head owns 2*nblk jobs,
 // alternately dK/dV and dQ, each sequence ordered from the most expensive
@@ -117,64 +131,86 @@ __device__ __forceinline__ Job job_of(const BwdParams& p) {
   return job;
 }
 
-// Four consecutive rows (r0 .. r0+3 of the tile starting at `row0`) of chunk
-// `ch`; rows past the end of the buffer read as zeros.
+// LDS of the grads launch (bytes). dK/dV jobs: Q and dO tiles plus the
+// tile's lse2 and D, two stages each; dQ jobs: K and V tiles, two stages.
 template <int D>
-__device__ __forceinline__ void load_rows4(__amdgpu_buffer_rsrc_t r, int row0, int r0, int ch,
-                                           uint4 w[4]) {
+struct GLayout {
+  static constexpr int kTileBytes = kTile * D * 2;
+  static constexpr int kA = 0;                    // Q (dK/dV) or K (dQ), stages 0, 1
+  static constexpr int kB = 2 * kTileBytes;       // dO (dK/dV) or V (dQ), stages 0, 1
+  static constexpr int kL = 4 * kTileBytes;       // lse2, stages 0, 1: 64 floats each
+  static constexpr int kR = kL + 2 * kTile * 4;   // D, stages 0, 1
+  static constexpr int kBytes = kR + 2 * kTile * 4;
+  static constexpr int kFill = kTileBytes / 1024 / kWaves;  // 1 KB blocks per wave and tile
+};
+
+// Per-lane LDS offsets shared by both jobs.
+template <int D>
+struct Offsets {
+  uint32_t row[D / 16];       // MFMA operand rows: row col (+32 per block), chunk 2kk + half
+  uint32_t tr[D / 32][2];     // transposing reads: d-block db, read 0/1 (+ 16-row bases)
+  uint32_t fill[GLayout<D>::kFill];
+  __device__ __forceinline__ void init(int wave, int lane) {
+    const int half = lane >> 5, col = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = load8<uint16_t>(r, (uint32_t)((row0 + r0 + i) * D + ch * 8));
+    for (int kk = 0; kk < D / 16; ++kk) row[kk] = row_offset<D>(col, 2 * kk + half);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd) tr[db][rd] = rows_t_offset<D>(db, rd, lane);
+#pragma unroll
+    for (int i = 0; i < GLayout<D>::kFill; ++i)
+      fill[i] = fill_lane_offset<D, kTile, kWaves>(i, wave, lane);
+  }
+};
+
+// Start loading rows row0 .. row0+63 of a head-sized bf16 tensor into `dst`.
+template <int D>
+__device__ __forceinline__ void fill_rows(unsigned char* dst, const uint16_t* g, int row0, int N,
+                                          const Offsets<D>& off, int wave) {
+  const auto r = make_rsrc(g + (size_t)row0 * D, (uint32_t)(N - row0) * D * 2u);
+  fill_direct<D, kTile, kWaves>(dst, r, off.fill, wave);
+}
+
+// Start loading 64 floats v[row0 .. row0+63] (zeros past N) into `dst`.
+__device__ __forceinline__ void fill_vec(unsigned char* dst, const float* g, int row0, int N,
+                                         int lane) {
+  const auto r = make_rsrc(g + row0, (uint32_t)(N - row0) * 4u);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)dst, 4, (uint32_t)lane * 4u, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- dK / dV
 
-template <int D>
-struct KVSmem {
-  uint16_t q[kTile * D];    // Q tile, row-major
-  uint16_t qt[D * kTile];   // Q tile, transposed
-  uint16_t g[kTile * D];    // dO tile, row-major
-  uint16_t gt[D * kTile];   // dO tile, transposed
-  float lse2[kTile];        // lse * log2(e); +inf past N
-  float dr[kTile];          // D_i; 0 past N
-};
-
-template <int D>
-struct QSmem {
-  uint16_t k[kTile * D];   // K tile, row-major
-  uint16_t kt[D * kTile];  // K tile, transposed
-  uint16_t v[kTile * D];   // V tile, row-major
-};
-
-template <int D>
-constexpr size_t kGradsSmem = sizeof(KVSmem<D>) > sizeof(QSmem<D>) ? sizeof(KVSmem<D>)
-                                                                     : sizeof(QSmem<D>);
-
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk, KVSmem<D>& sm) {
+__device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
+                                         unsigned char* smem) {
+  using LY = GLayout<D>;
   constexpr int kDK = D / 16;
   constexpr int kDB = D / 32;
-  constexpr int kChunks = D / 8;
-  constexpr int kGroups = (kTile / 4) * kChunks;  // (4-row group, chunk) pairs per tile
-  static_assert(kGroups <= kThreads, "one staging group per thread at most");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int N = p.N;
   const size_t head = (size_t)bh * N;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const auto qr = make_rsrc(p.q + head * D, head_bytes);
-  const auto gr = make_rsrc(p.dout + head * D, head_bytes);
+  const uint16_t* qg = p.q + head * D;
+  const uint16_t* gg = p.dout + head * D;
+  const float* lg = p.lse2 + head;
+  const float* rg = p.drow + head;
 
   const int k0 = kblk * kBlock;
   const int kw0 = k0 + wave * 32;  // this wave's first key
   const int mykey = kw0 + col;
 
-  // K^T and V^T columns of this lane's key, as B operands
+  Offsets<D> off;
+  off.init(wave, lane);
+
+  // K^T and V^T columns of this lane's key, as B operands (zeros past N)
   bf16x8 kreg[kDK], vreg[kDK];
   {
-    const auto kr = make_rsrc(p.k + head * D, head_bytes);
-    const auto vr = make_rsrc(p.v + head * D, head_bytes);
+    const uint32_t bytes = (uint32_t)N * D * 2u;
+    const auto kr = make_rsrc(p.k + head * D, bytes);
+    const auto vr = make_rsrc(p.v + head * D, bytes);
 #pragma unroll
     for (int kk = 0; kk < kDK; ++kk) {
       const uint32_t e = (uint32_t)(mykey * D + kk * 16 + half * 8);
@@ -192,63 +228,58 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk, K
   const int ntiles = (N + kTile - 1) / kTile;
   const int t0 = CAUSAL ? k0 / kTile : 0;  // earlier query rows see none of these keys
   const float c = p.c;
-  const int sg = tid / kChunks, sch = tid % kChunks;  // staging group of this thread
 
-  // registers holding the next tile while the current one is computed
-  uint4 wq[4], wg[4];
-  float l2 = 0.0f, dr = 0.0f;
-  auto fetch = [&](int t) {
-    const int qs = t * kTile;
-    if (tid < kGroups) {  // wave-uniform
-      load_rows4<D>(qr, qs, 4 * sg, sch, wq);
-      load_rows4<D>(gr, qs, 4 * sg, sch, wg);
-    }
-    if (tid < kTile) {
-      const int row = qs + tid;
-      l2 = row < N ? p.lse[head + row] * kLog2e : INFINITY;
-      dr = row < N ? p.drow[head + row] : 0.0f;
-    }
+  auto fill = [&](int t) {
+    const int st = t & 1, r0 = t * kTile;
+    fill_rows<D>(smem + LY::kA + st * LY::kTileBytes, qg, r0, N, off, wave);
+    fill_rows<D>(smem + LY::kB + st * LY::kTileBytes, gg, r0, N, off, wave);
+    if (wave == 0) fill_vec(smem + LY::kL + st * kTile * 4, lg, r0, N, lane);
+    if (wave == 1) fill_vec(smem + LY::kR + st * kTile * 4, rg, r0, N, lane);
   };
-  if (t0 < ntiles) fetch(t0);
 
+  if (t0 < ntiles) fill(t0);
   for (int t = t0; t < ntiles; ++t) {
-    const int qs = t * kTile;
-    __syncthreads();  // the previous tile is no longer read
-    if (tid < kGroups) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        st_row<D>(sm.q, 4 * sg + r, sch, wq[r]);
-        st_row<D>(sm.g, 4 * sg + r, sch, wg[r]);
-      }
-      st_tr4<kTile>(sm.qt, 4 * sg, sch, wq);
-      st_tr4<kTile>(sm.gt, 4 * sg, sch, wg);
-    }
-    if (tid < kTile) {
-      sm.lse2[tid] = l2;
-      sm.dr[tid] = dr;
-    }
+    // tile t is in LDS for every wave, and every wave is done with tile t-1,
+    // whose stage the loads of tile t+1 overwrite
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);
+    if (t + 1 < ntiles) fill(t + 1);
 
+    const int qs = t * kTile;
     if (CAUSAL && qs + kTile - 1 < kw0) continue;  // every row of the tile precedes our keys
     const bool need_mask = CAUSAL && qs < kw0 + 31;
+    const int st = t & 1;
+    const unsigned char* qt = smem + LY::kA + st * LY::kTileBytes;
+    const unsigned char* gt = smem + LY::kB + st * LY::kTileBytes;
+    const float* l2t = reinterpret_cast<const float*>(smem + LY::kL + st * kTile * 4);
+    const float* drt = reinterpret_cast<const float*>(smem + LY::kR + st * kTile * 4);
 
+    // ---- S = Q K^T and dP = dO V^T: rows = the tile's queries, column = key
     uint32_t pk[2][8], dsk[2][8];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s = zero16(), dp = zero16();
-      const int row = qb * 32 + col;
+      bf16x8 qa[kDK], ga[kDK];
 #pragma unroll
       for (int kk = 0; kk < kDK; ++kk) {
-        s = mfma32(ld_row<D>(sm.q, row, 2 * kk + half), kreg[kk], s);
-        dp = mfma32(ld_row<D>(sm.g, row, 2 * kk + half), vreg[kk], dp);
+        qa[kk] = lds_ld16(qt + qb * 32 * D * 2 + off.row[kk]);
+        ga[kk] = lds_ld16(gt + qb * 32 * D * 2 + off.row[kk]);
       }
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < kDK; ++kk) {
+        s = mfma32(qa[kk], kreg[kk], s);
+        dp = mfma32(ga[kk], vreg[kk], dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDK, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kDK, 0);
+
+      // ---- P = 2^(c*S - lse2) and dS = P * (dP - D), packed to bf16
       float pv[16], dsv[16];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int r0 = qb * 32 + 8 * g4 + 4 * half;  // tile rows of elements 4g4..4g4+3
-        const f32x4 l2v = *reinterpret_cast<const f32x4*>(&sm.lse2[r0]);
-        const f32x4 drv = *reinterpret_cast<const f32x4*>(&sm.dr[r0]);
+        const f32x4 l2v = *reinterpret_cast<const f32x4*>(&l2t[r0]);
+        const f32x4 drv = *reinterpret_cast<const f32x4*>(&drt[r0]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * g4 + i;
@@ -265,20 +296,30 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk, K
       }
     }
 
+    // ---- dV^T += dO^T P and dK^T += Q^T dS; slots (qb, m) are accumulator
+    // rows 8m..8m+7 of S, i.e. tile rows 32qb + 16m + ...
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
+        const int rb = (qb * 32 + m * 16) * D * 2;
+        bf16x8 ga[kDB], qa[kDB];
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          ga[db] = lds_tr_pair(gt + rb + off.tr[db][0], gt + rb + off.tr[db][1]);
+          qa[db] = lds_tr_pair(qt + rb + off.tr[db][0], qt + rb + off.tr[db][1]);
+        }
         const uint4 pu = {pk[qb][4 * m], pk[qb][4 * m + 1], pk[qb][4 * m + 2], pk[qb][4 * m + 3]};
         const uint4 du = {dsk[qb][4 * m], dsk[qb][4 * m + 1], dsk[qb][4 * m + 2],
                           dsk[qb][4 * m + 3]};
         const bf16x8 pb = as_bf16x8(pu), db8 = as_bf16x8(du);
-        const int chunk = 4 * qb + 2 * m + half;
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
-          dvacc[db] = mfma32(ld_tr<kTile>(sm.gt, db * 32 + col, chunk), pb, dvacc[db]);
-          dkacc[db] = mfma32(ld_tr<kTile>(sm.qt, db * 32 + col, chunk), db8, dkacc[db]);
+          dvacc[db] = mfma32(ga[db], pb, dvacc[db]);
+          dkacc[db] = mfma32(qa[db], db8, dkacc[db]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * kDB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kDB, 0);
       }
   }
 
@@ -304,31 +345,34 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk, K
 // ---------------------------------------------------------------- dQ
 
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk, QSmem<D>& sm) {
+__device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
+                                       unsigned char* smem) {
+  using LY = GLayout<D>;
   constexpr int kDK = D / 16;
   constexpr int kDB = D / 32;
-  constexpr int kChunks = D / 8;
-  constexpr int kGroups = (kTile / 4) * kChunks;
-  static_assert(kGroups <= kThreads, "one staging group per thread at most");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int N = p.N;
   const size_t head = (size_t)bh * N;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const auto kr = make_rsrc(p.k + head * D, head_bytes);
-  const auto vr = make_rsrc(p.v + head * D, head_bytes);
+  const uint16_t* kg = p.k + head * D;
+  const uint16_t* vg = p.v + head * D;
 
   const int q0 = qblk * kBlock;
   const int qw0 = q0 + wave * 32;
   const int myq = qw0 + col;
   const int wave_last = min(qw0 + 32, N) - 1;
 
-  bf16x8 qreg[kDK], greg[kDK];  // Q^T and dO^T columns of this lane's row
-  float l2 = INFINITY, dr = 0.0f;
+  Offsets<D> off;
+  off.init(wave, lane);
+
+  bf16x8 qreg[kDK], greg[kDK];  // Q^T and dO^T columns of this lane's row (zeros past N)
+  float l2 = 0.0f, dr = 0.0f;
   {
-    const auto qr = make_rsrc(p.q + head * D, head_bytes);
-    const auto gr = make_rsrc(p.dout + head * D, head_bytes);
+    const uint32_t bytes = (uint32_t)N * D * 2u;
+    const auto qr = make_rsrc(p.q + head * D, bytes);
+    const auto gr = make_rsrc(p.dout + head * D, bytes);
 #pragma unroll
     for (int kk = 0; kk < kDK; ++kk) {
       const uint32_t e = (uint32_t)(myq * D + kk * 16 + half * 8);
@@ -336,7 +380,7 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk, QSm
       greg[kk] = as_bf16x8(load8<uint16_t>(gr, e));
     }
     if (myq < N) {
-      l2 = p.lse[head + myq] * kLog2e;
+      l2 = p.lse2[head + myq];
       dr = p.drow[head + myq];
     }
   }
@@ -347,51 +391,50 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk, QSm
   const int ntiles_all = (N + kTile - 1) / kTile;
   const int ntiles = CAUSAL ? min(ntiles_all, (min(q0 + kBlock, N) - 1) / kTile + 1) : ntiles_all;
   const float c = p.c;
-  const int sg = tid / kChunks, sch = tid % kChunks;
 
-  uint4 wk[4], wv[4];
-  auto fetch = [&](int t) {
-    if (tid < kGroups) {  // wave-uniform
-      load_rows4<D>(kr, t * kTile, 4 * sg, sch, wk);
-      load_rows4<D>(vr, t * kTile, 4 * sg, sch, wv);
-    }
+  auto fill = [&](int t) {
+    const int st = t & 1, r0 = t * kTile;
+    fill_rows<D>(smem + LY::kA + st * LY::kTileBytes, kg, r0, N, off, wave);
+    fill_rows<D>(smem + LY::kB + st * LY::kTileBytes, vg, r0, N, off, wave);
   };
-  fetch(0);
 
+  fill(0);
   for (int t = 0; t < ntiles; ++t) {
-    const int key0 = t * kTile;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid < kGroups) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        st_row<D>(sm.k, 4 * sg + r, sch, wk[r]);
-        st_row<D>(sm.v, 4 * sg + r, sch, wv[r]);
-      }
-      st_tr4<kTile>(sm.kt, 4 * sg, sch, wk);
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);
+    if (t + 1 < ntiles) fill(t + 1);
 
+    const int key0 = t * kTile;
     if (CAUSAL && key0 > wave_last) continue;
-    const bool need_mask = (key0 + kTile > N) || (CAUSAL && key0 + kTile - 1 > qw0);
+    const bool need_mask = CAUSAL && key0 + kTile - 1 > qw0;
+    const int st = t & 1;
+    const unsigned char* kt = smem + LY::kA + st * LY::kTileBytes;
+    const unsigned char* vt = smem + LY::kB + st * LY::kTileBytes;
 
     uint32_t dsk[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
-      const int row = kb * 32 + col;
+      bf16x8 ka[kDK], va[kDK];
 #pragma unroll
       for (int kk = 0; kk < kDK; ++kk) {
-        s = mfma32(ld_row<D>(sm.k, row, 2 * kk + half), qreg[kk], s);
-        dp = mfma32(ld_row<D>(sm.v, row, 2 * kk + half), greg[kk], dp);
+        ka[kk] = lds_ld16(kt + kb * 32 * D * 2 + off.row[kk]);
+        va[kk] = lds_ld16(vt + kb * 32 * D * 2 + off.row[kk]);
       }
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < kDK; ++kk) {
+        s = mfma32(ka[kk], qreg[kk], s);
+        dp = mfma32(va[kk], greg[kk], dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDK, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kDK, 0);
       float dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pr = fast_exp2(__builtin_fmaf(s[r], c, -l2));
         if (need_mask) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          pr = (key < N && (!CAUSAL || key <= myq)) ? pr : 0.0f;
+          pr = key <= myq ? pr : 0.0f;
         }
         dsv[r] = pr * (dp[r] - dr);
       }
@@ -399,17 +442,23 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk, QSm
       for (int j = 0; j < 8; ++j) dsk[kb][j] = pack_bf16x2(dsv[2 * j], dsv[2 * j + 1]);
     }
 
+    // ---- dQ^T += K^T dS^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
+        const int rb = (kb * 32 + m * 16) * D * 2;
+        bf16x8 ka[kDB];
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+          ka[db] = lds_tr_pair(kt + rb + off.tr[db][0], kt + rb + off.tr[db][1]);
         const uint4 du = {dsk[kb][4 * m], dsk[kb][4 * m + 1], dsk[kb][4 * m + 2],
                           dsk[kb][4 * m + 3]};
         const bf16x8 b = as_bf16x8(du);
-        const int chunk = 4 * kb + 2 * m + half;
 #pragma unroll
-        for (int db = 0; db < kDB; ++db)
-          dqacc[db] = mfma32(ld_tr<kTile>(sm.kt, db * 32 + col, chunk), b, dqacc[db]);
+        for (int db = 0; db < kDB; ++db) dqacc[db] = mfma32(ka[db], b, dqacc[db]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kDB, 0);
       }
   }
 
@@ -430,12 +479,12 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk, QSm
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kGradsSmem<D>];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[GLayout<D>::kBytes];
   const Job job = job_of<CAUSAL>(p);
   if (job.is_dq)
-    dq_job<D, CAUSAL>(p, job.bh, job.blk, *reinterpret_cast<QSmem<D>*>(smem));
+    dq_job<D, CAUSAL>(p, job.bh, job.blk, smem);
   else
-    dkdv_job<D, CAUSAL>(p, job.bh, job.blk, *reinterpret_cast<KVSmem<D>*>(smem));
+    dkdv_job<D, CAUSAL>(p, job.bh, job.blk, smem);
 }
 
 template <int D>
@@ -445,8 +494,8 @@ BwdParams make_params(const BwdArgs& a) {
   p.k = static_cast<const uint16_t*>(a.k);
   p.v = static_cast<const uint16_t*>(a.v);
   p.dout = static_cast<const uint16_t*>(a.dout);
-  p.lse = a.lse;
   p.drow = a.drow;
+  p.lse2 = a.drow + (size_t)a.B * a.H * a.N;
   p.dq = static_cast<uint16_t*>(a.dq);
   p.dk = static_cast<uint16_t*>(a.dk);
   p.dv = static_cast<uint16_t*>(a.dv);
@@ -464,9 +513,9 @@ hipError_t launch_prep_typed(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.H * a.N;
   constexpr int kRowsPerBlock = kThreads / (D / 8);
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  hipLaunchKernelGGL((bwd_rows_kernel<D>), grid, dim3(kThreads), 0, a.stream,
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), grid, dim3(kThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
-                     a.drow, rows);
+                     a.lse, a.drow, a.drow + rows, rows);
   return hipGetLastError();
 }
 

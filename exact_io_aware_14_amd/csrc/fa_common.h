@@ -107,8 +107,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // LDS tiles. A tile of R rows x D columns of bf16 is kept in one of two forms:
 //
 // * row-major [row][d]: the 16-byte chunk c of row r sits at chunk position
-//   c ^ (r & 7), so that the 32 lanes that read one chunk column of 32
-//   consecutive rows (an MFMA A or B operand) hit different banks;
+//   c ^ rsw(r). The LDS serves 16 lanes of a 16-byte read per clock from 64
+//   banks (256 bytes), and an MFMA operand read has 16 consecutive rows per
+//   clock reading the same chunk c: rsw spreads those 16 reads over all 256
+//   bytes (d = 128: a row is 256 bytes, rsw = r & 15; d = 64: a row is 128
+//   bytes, r & 1 picks the half, rsw = (r >> 1) & 7 the chunk);
 // * transposed [d][pos(row)]: each LDS row holds one column d of the tile.
 //   Rows are stored at position pos(r), r with bits 2 and 3 swapped, which
 //   makes the eight rows one lane needs for one MFMA operand (see below)
@@ -131,16 +134,33 @@ __device__ __forceinline__ int tpos(int r) {
 // Chunk swizzle of column d of a transposed tile.
 __device__ __forceinline__ int tsw(int d) { return (d ^ (d >> 3)) & 7; }
 
+// Chunk swizzle of row r of a row-major tile of width D. It serves both
+// read patterns used on these tiles:
+//   (a) an MFMA operand read: 16 consecutive rows (a multiple of 16 first),
+//       the same 16-byte chunk -> 16 distinct positions of the 256 bytes;
+//   (b) a transposing read (below): 4 consecutive rows (a multiple of 4
+//       first) x 4 consecutive chunks (a multiple of 4 first) -> 16
+//       distinct positions.
+// d = 128 (256-byte rows): bits 2-3 of the swizzle come from r & 3 (they
+// separate the rows of (b) while the chunk varies bits 0-1) and bits 0-1
+// from (r >> 2) & 3, completing (a). d = 64 (128-byte rows, r & 1 picks the
+// half of the bank space): bit 2 from (r >> 1) & 1, bits 0-1 from (r >> 2) & 3.
+template <int D>
+__device__ __forceinline__ int rsw(int r) {
+  static_assert(D == 64 || D == 128, "tile width");
+  return D == 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+}
+
 // Store chunk `ch` (8 elements) of row `row` into a row-major tile of width D.
 template <int D>
 __device__ __forceinline__ void st_row(uint16_t* tile, int row, int ch, uint4 val) {
-  *reinterpret_cast<uint4*>(&tile[row * D + ((ch ^ (row & 7)) * 8)]) = val;
+  *reinterpret_cast<uint4*>(&tile[row * D + ((ch ^ rsw<D>(row)) * 8)]) = val;
 }
 
 // MFMA operand read: chunk `ch` of row `row` of a row-major tile.
 template <int D>
 __device__ __forceinline__ bf16x8 ld_row(const uint16_t* tile, int row, int ch) {
-  return *reinterpret_cast<const bf16x8*>(&tile[row * D + ((ch ^ (row & 7)) * 8)]);
+  return *reinterpret_cast<const bf16x8*>(&tile[row * D + ((ch ^ rsw<D>(row)) * 8)]);
 }
 
 // Store four consecutive rows r0..r0+3 (r0 % 4 == 0) of chunk `ch` (columns
@@ -162,6 +182,126 @@ __device__ __forceinline__ void st_tr4(uint16_t* tile, int r0, int ch, const uin
     const int d0 = ch * 8 + 2 * j, d1 = d0 + 1;
     *reinterpret_cast<uint2*>(&tile[d0 * R + (((pos >> 3) ^ tsw(d0)) * 8) + (pos & 7)]) = lo;
     *reinterpret_cast<uint2*>(&tile[d1 * R + (((pos >> 3) ^ tsw(d1)) * 8) + (pos & 7)]) = hi;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row-major tiles read through the transposing LDS read. ds_read_b64_tr_b16
+// works on groups of 16 lanes: lane j of a group points at 4 consecutive
+// bf16 (a "row" of 4), and lane i of the group receives element i % 4 of the
+// rows pointed at by lanes i/4, i/4+4, i/4+8 and i/4+12. With lane j pointing
+// at tile row k0 + j/4, columns d0 + 4*(j%4) .. +3, lane i receives column
+// d0 + i of rows k0 .. k0+3: four consecutive tile rows of one column, which
+// is an MFMA operand whose k-slots run along the tile rows.
+//
+// These tiles use the same swizzle rsw as MFMA row reads. Shifting the row by
+// a multiple of 16 keeps rsw; within ld_rows_t the second read's rows are 8
+// further on, which rows_t_offset accounts for.
+// ---------------------------------------------------------------------------
+
+#define FA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ bf16x4 tr_read(const uint16_t* p) {
+  typedef __bf16 v4bf __attribute__((__vector_size__(4 * sizeof(__bf16))));
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                        (FA_LDS v4bf*)(const_cast<uint16_t*>(p))));
+}
+
+// Byte offset, within a row-major tile of width D read through tr_read, of
+// this lane's pointer for read `rd` (0: k-slots 0-3, 1: k-slots 4-7) of the
+// MFMA operand of ld_rows_t with kbase = 0 and d-block db. A kbase that is a
+// multiple of 16 adds kbase rows (rsw repeats every 16 rows).
+template <int D>
+__device__ __forceinline__ uint32_t rows_t_offset(int db, int rd, int lane) {
+  const int g = lane >> 4, j = lane & 15, h = lane >> 5;
+  const int d0 = db * 32 + 16 * (g & 1) + 4 * (j & 3);
+  const int r = 4 * h + (j >> 2) + 8 * rd;
+  return (uint32_t)(r * D + (((d0 >> 3) ^ rsw<D>(r)) << 3) + (d0 & 7)) * 2u;
+}
+
+// Byte offset, within a row-major tile of width D (swizzle rsw), of chunk ch
+// of row `row`.
+template <int D>
+__device__ __forceinline__ uint32_t row_offset(int row, int ch) {
+  return (uint32_t)(row * D + ((ch ^ rsw<D>(row)) << 3)) * 2u;
+}
+
+__device__ __forceinline__ bf16x8 lds_ld16(const unsigned char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Two transposing reads form one operand (slots 0-3 from p0, 4-7 from p1).
+__device__ __forceinline__ bf16x8 lds_tr_pair(const unsigned char* p0, const unsigned char* p1) {
+  const bf16x4 a = tr_read(reinterpret_cast<const uint16_t*>(p0));
+  const bf16x4 b = tr_read(reinterpret_cast<const uint16_t*>(p1));
+  bf16x8 v;
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  return v;
+}
+
+// MFMA operand from a row-major tile (swizzle rsw) whose k-slots run along
+// the tile rows: lane (h, c) gets column 32*db + c, and slot s stands for tile
+// row kbase + 8*(s/4) + 4h + (s%4) -- the row order of the repacked
+// accumulator (see above), so P^T or dS^T built from an accumulator pairs
+// with it slot for slot.
+template <int D>
+__device__ __forceinline__ bf16x8 ld_rows_t(const uint16_t* tile, int kbase, int db, int lane) {
+  const int g = lane >> 4, j = lane & 15, h = lane >> 5;
+  const int d0 = db * 32 + 16 * (g & 1) + 4 * (j & 3);
+  const int r0 = kbase + 4 * h + (j >> 2);
+  const int r1 = r0 + 8;
+  const bf16x4 a = tr_read(tile + r0 * D + (((d0 >> 3) ^ rsw<D>(r0)) << 3) + (d0 & 7));
+  const bf16x4 b = tr_read(tile + r1 * D + (((d0 >> 3) ^ rsw<D>(r1)) << 3) + (d0 & 7));
+  bf16x8 v;
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  return v;
+}
+
+// Fill ROWS rows of a row-major bf16 tile (width D) straight from global
+// memory into LDS, 16 bytes per lane, with no registers in between: each of
+// the WAVES waves moves whole 1 KB blocks (one buffer_load ... lds each); the
+// swizzle is applied on the global side (lane l of a block takes the chunk
+// that belongs at LDS position 16*l). `r` views the rows from the tile's
+// first row on; rows past its end are written as zeros. `wave` must be
+// wave-uniform.
+template <int D, int ROWS, int WAVES>
+__device__ __forceinline__ uint32_t fill_lane_offset(int i, int wave, int lane) {
+  constexpr int kRowBytes = D * 2;
+  constexpr int kPerWave = ROWS * kRowBytes / 1024 / WAVES;
+  constexpr int kRowsPerBlock = 1024 / kRowBytes;
+  const int b = wave * kPerWave + i;
+  const int row = b * kRowsPerBlock + (lane * 16) / kRowBytes;
+  const int pos = ((lane * 16) % kRowBytes) / 16;
+  const int ch = pos ^ rsw<D>(row);
+  return (uint32_t)(row * kRowBytes + ch * 16);
+}
+
+template <int D, int ROWS, int WAVES>
+__device__ __forceinline__ void fill_direct(unsigned char* tile, __amdgpu_buffer_rsrc_t r,
+                                            const uint32_t* lane_off, int wave) {
+  constexpr int kPerWave = ROWS * D * 2 / 1024 / WAVES;
+  static_assert(ROWS * D * 2 % (1024 * WAVES) == 0, "blocks must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (FA_LDS void*)(tile + (wave * kPerWave + i) * 1024), 16, lane_off[i], 0, 0, 0);
+}
+
+// The same tile filled through registers from fp32 rows (rounded to bf16).
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void fill_f32(uint16_t* tile, __amdgpu_buffer_rsrc_t r, int row0,
+                                         int tid) {
+  constexpr int kChunks = D / 8;
+  static_assert(ROWS * kChunks % THREADS == 0, "chunks must split evenly");
+#pragma unroll
+  for (int i = 0; i < ROWS * kChunks / THREADS; ++i) {
+    const int id = tid + i * THREADS;
+    const int row = id / kChunks, ch = id % kChunks;
+    const uint4 val = load8<float>(r, (uint32_t)((row0 + row) * D + ch * 8));
+    const int pos = ch ^ rsw<D>(row);
+    *reinterpret_cast<uint4*>(&tile[row * D + pos * 8]) = val;
   }
 }
 

@@ -1,5 +1,5 @@
 // Forward exact attention for gfx950: one workgroup per (batch, head, block
-// of 128 query rows), four waves of 32 query rows each.
+// of 256 query rows), eight waves of 32 query rows each.
 //
 // Method: the tiled forward with a running row maximum m and row sum l, in
 // which the partial output of earlier key tiles is rescaled whenever m grows
@@ -20,19 +20,33 @@
 // the accumulator) and holds 16 of the tile's scores per 32 keys; the two
 // halves of the wave hold the other keys of the same rows. The probabilities
 // are packed to bf16 in the lane and feed the product O^T += V^T P^T
-// directly as its B operand; V is kept transposed in LDS to serve as the A
-// operand.
+// directly as its B operand; the A operand V^T comes from the row-major V
+// tile through the transposing LDS read.
+//
+// K and V tiles move from global memory into LDS with buffer loads that
+// write LDS directly (no registers, no VALU), double-buffered and issued two
+// phases ahead of their first use. fp32 inputs take the same path through
+// registers, rounded to bf16.
+//
+// Schedule ("ping-pong"): the eight waves form two groups of four, one wave
+// of each group per SIMD. Work alternates between an MFMA phase X(t) =
+// {O += V_{t-1}^T P_{t-1}, S_t = K_t Q^T} and a VALU phase V(t) = {masks,
+// online softmax of S_t, P_t}, and the second group runs one phase behind
+// the first, with a workgroup barrier between phases: while one wave of a
+// SIMD issues its MFMAs (at raised priority) the other computes its
+// softmax, so the matrix cores and the vector ALUs work at the same time
+// (the interleaving principle the deepfa.ir page describes for
+// FlashAttention-3, here across waves of one SIMD rather than asynchronous
+// tensor-core instructions).
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
-constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
-constexpr int kBC = 64;                     // keys per tile
-constexpr int kThreads = kWaves * 64;
 // A row maximum may exceed the reference used for the exponentials by up to
 // this many powers of two before the accumulators are rescaled; the
 // probabilities then stay below 2^8, far inside fp32 and bf16 range.
@@ -52,66 +66,48 @@ struct FwdParams {
   int xcd_remap; // heads grouped per XCD (requires BH % 8 == 0)
 };
 
-template <int D>
-struct Smem {
-  uint16_t k[kBC * D];   // K tile, row-major
-  uint16_t vt[D * kBC];  // V tile, transposed
+template <int D, int BC, int WAVES>
+struct Layout {
+  static constexpr int kTileBytes = BC * D * 2;
+  static constexpr int kK = 0;                // K stages 0, 1 (row-major, rsw)
+  static constexpr int kV = 2 * kTileBytes;   // V stages 0, 1 (row-major, rsw)
+  static constexpr int kBytes = 4 * kTileBytes;
+  static constexpr int kFill = kTileBytes / 1024 / WAVES;  // 1 KB blocks per wave and tile
+  static_assert(kFill >= 1 && kTileBytes % (1024 * WAVES) == 0, "tile must split over waves");
 };
 
-template <int D, typename TIn>
-struct TileLoader {
-  static constexpr int kChunks = D / 8;                       // 16-byte chunks per row
-  static constexpr int kKLoads = kBC * kChunks / kThreads;    // K chunks per thread
-  static constexpr int kVGroups = (kBC / 4) * kChunks;        // (4-key group, chunk) pairs
-  static constexpr int kVLoads = (kVGroups + kThreads - 1) / kThreads;
-  static_assert(kBC * kChunks % kThreads == 0, "K tile must split evenly");
+// Workgroup shapes. kSequential: 4 waves (128 query rows), two workgroups per
+// CU, each wave running its tiles as MFMA -> VALU -> MFMA; the two waves a
+// SIMD holds belong to different workgroups and overlap freely.
+// kPingPong: 8 waves (256 rows) in two groups of four, one wave of each
+// group per SIMD (waves w and w+4 share a SIMD), the groups one phase apart
+// at workgroup barriers so that one wave's MFMA phase meets the other's VALU
+// phase.
+enum Schedule { kSequential = 4, kPingPong = 8 };
 
-  uint4 kreg[kKLoads];
-  uint4 vreg[kVLoads][4];
-
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                       int key0, int tid) {
-#pragma unroll
-    for (int i = 0; i < kKLoads; ++i) {
-      const int id = tid + i * kThreads;
-      kreg[i] = load8<TIn>(kr, (uint32_t)((key0 + id / kChunks) * D + (id % kChunks) * 8));
-    }
-#pragma unroll
-    for (int i = 0; i < kVLoads; ++i) {
-      const int id = tid + i * kThreads;
-      if (id < kVGroups) {  // wave-uniform
-        const int ch = id % kChunks, g = id / kChunks;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vreg[i][r] = load8<TIn>(vr, (uint32_t)((key0 + 4 * g + r) * D + ch * 8));
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(Smem<D>& sm, int tid) {
-#pragma unroll
-    for (int i = 0; i < kKLoads; ++i) {
-      int id = tid + i * kThreads;
-      st_row<D>(sm.k, id / kChunks, id % kChunks, kreg[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < kVLoads; ++i) {
-      int id = tid + i * kThreads;
-      if (id < kVGroups) st_tr4<kBC>(sm.vt, 4 * (id / kChunks), id % kChunks, vreg[i]);
-    }
-  }
+template <int WAVES>
+struct Shape {
+  static constexpr int kThreads = WAVES * 64;
+  static constexpr int kBR = WAVES * kRowsPerWave;  // query rows per workgroup
+  static constexpr int kMinBlocks = WAVES == kPingPong ? 1 : 2;
 };
 
-template <int D, bool CAUSAL, typename TIn, typename TOut>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
-  __shared__ Smem<D> sm;
-  constexpr int kDK = D / 16;  // MFMA steps along d for S^T
-  constexpr int kDB = D / 32;  // 32-row blocks of O^T
-  constexpr int kKB = kBC / 32;
+template <int D, int BC, int WAVES, bool CAUSAL, typename TIn, typename TOut>
+__global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) void fwd_kernel(
+    FwdParams p) {
+  using LY = Layout<D, BC, WAVES>;
+  constexpr int kBR = Shape<WAVES>::kBR;
+  constexpr int kThreads = Shape<WAVES>::kThreads;
+  constexpr int kRowsPerGroup = 4 * kRowsPerWave;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LY::kBytes];
+  constexpr int kDK = D / 16;   // MFMA steps along d for S^T
+  constexpr int kDB = D / 32;   // 32-row blocks of O^T
+  constexpr int kKB = BC / 32;  // 32-key blocks of a tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // ping-pong: 0 leads, 1 follows one phase behind
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -132,24 +128,41 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   const int qb = CAUSAL ? (p.nqb - 1 - qbr) : qbr;
   const int N = p.N;
   const size_t head_off = (size_t)bh * (size_t)N * D;
-  // buffer views of this head; reads past row N return zeros
-  const uint32_t head_bytes = (uint32_t)N * D * sizeof(TIn);
-  const auto qr = make_rsrc(reinterpret_cast<const TIn*>(p.q) + head_off, head_bytes);
-  const auto kr = make_rsrc(reinterpret_cast<const TIn*>(p.k) + head_off, head_bytes);
-  const auto vr = make_rsrc(reinterpret_cast<const TIn*>(p.v) + head_off, head_bytes);
+  const TIn* qg = reinterpret_cast<const TIn*>(p.q) + head_off;
+  const TIn* kg = reinterpret_cast<const TIn*>(p.k) + head_off;
+  const TIn* vg = reinterpret_cast<const TIn*>(p.v) + head_off;
 
-  const int q0 = qb * kBR;                        // first row of the block
-  const int qw0 = q0 + wave * kRowsPerWave;       // first row of this wave
-  const int myq = qw0 + col;                      // this lane's row
+  const int q0 = qb * kBR;                                        // first row of the block
+  const int qw0 = q0 + grp * kRowsPerGroup + (wave & 3) * kRowsPerWave;  // this wave's
+  const int myq = qw0 + col;                                      // this lane's row
   const int wave_last = min(qw0 + kRowsPerWave, N) - 1;
 
   // ---- Q^T as the B operand of S^T = K Q^T: column = row myq, k-slots = d
   bf16x8 qreg[kDK];
+  {
+    const auto qr = make_rsrc(qg, (uint32_t)N * D * sizeof(TIn));  // rows past N read 0
 #pragma unroll
-  for (int kk = 0; kk < kDK; ++kk) {
-    uint4 u = load8<TIn>(qr, (uint32_t)(myq * D + kk * 16 + half * 8));
-    if (p.negate_q) u = negate8(u);
-    qreg[kk] = as_bf16x8(u);
+    for (int kk = 0; kk < kDK; ++kk) {
+      uint4 u = load8<TIn>(qr, (uint32_t)(myq * D + kk * 16 + half * 8));
+      if (p.negate_q) u = negate8(u);
+      qreg[kk] = as_bf16x8(u);
+    }
+  }
+
+  // ---- per-lane LDS offsets, fixed for the whole loop
+  uint32_t koff[kDK];  // K operand of S^T: row col (+32 kb), chunk 2kk + half
+#pragma unroll
+  for (int kk = 0; kk < kDK; ++kk) koff[kk] = row_offset<D>(col, 2 * kk + half);
+  uint32_t voff[kDB][2];  // V^T operand: d-block db, read 0/1 (+ rows kb*32 + m*16)
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) voff[db][rd] = rows_t_offset<D>(db, rd, lane);
+  uint32_t fk[LY::kFill], fv[LY::kFill];  // direct-fill offsets of this lane
+#pragma unroll
+  for (int i = 0; i < LY::kFill; ++i) {
+    fk[i] = fill_lane_offset<D, BC, WAVES>(i, wave, lane);
+    fv[i] = fill_lane_offset<D, BC, WAVES>(i, wave, lane);
   }
 
   f32x16 oacc[kDB];
@@ -157,36 +170,79 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   for (int i = 0; i < kDB; ++i) oacc[i] = zero16();
   float m_run = -INFINITY;  // reference maximum, in units of log2 (scale*log2e*score)
   float l_run = 0.0f;       // this lane's part of the row sum
+  f32x16 s[kKB];            // S^T of the tile between its MFMA and VALU phases
+  uint32_t pk[kKB][8];      // P^T packed to bf16, between its VALU and MFMA phases
 
-  const int ktiles_all = (N + kBC - 1) / kBC;
-  const int ktiles = CAUSAL ? min(ktiles_all, (min(q0 + kBR, N) - 1) / kBC + 1) : ktiles_all;
+  const int ktiles_all = (N + BC - 1) / BC;
+  // tiles the workgroup walks, and tiles with a visible key for this wave
+  const int ntiles = CAUSAL ? min(ktiles_all, (min(q0 + kBR, N) - 1) / BC + 1) : ktiles_all;
+  const int wtiles = qw0 >= N ? 0 : (CAUSAL ? wave_last / BC + 1 : ktiles_all);
   const float c = p.c;
 
-  TileLoader<D, TIn> ld;
-  ld.load(kr, vr, 0, tid);
-
-  for (int t = 0; t < ktiles; ++t) {
-    __syncthreads();  // every wave is done reading the previous tile
-    ld.store(sm, tid);
-    __syncthreads();
-    if (t + 1 < ktiles) ld.load(kr, vr, (t + 1) * kBC, tid);
-
-    const int key0 = t * kBC;
-    if (CAUSAL && key0 > wave_last) continue;  // no visible key for this wave
-
-    // ---- S^T = K Q^T for the BC keys of the tile
-    f32x16 s[kKB];
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) {
-      s[kb] = zero16();
-      const int row = kb * 32 + col;
-#pragma unroll
-      for (int kk = 0; kk < kDK; ++kk)
-        s[kb] = mfma32(ld_row<D>(sm.k, row, 2 * kk + half), qreg[kk], s[kb]);
+  auto fill_tile = [&](const TIn* g, int t, int base, const uint32_t* lane_off) {
+    const int key0 = t * BC;
+    const auto r = make_rsrc(g + (size_t)key0 * D, (uint32_t)(N - key0) * D * sizeof(TIn));
+    unsigned char* dst = smem + base + (t & 1) * LY::kTileBytes;
+    if constexpr (sizeof(TIn) == 2) {
+      fill_direct<D, BC, WAVES>(dst, r, lane_off, wave);
+    } else {
+      fill_f32<D, BC, kThreads>(reinterpret_cast<uint16_t*>(dst), r, 0, tid);
     }
+  };
 
-    // ---- masks: keys past N, and keys after the row for causal
-    const bool need_mask = (key0 + kBC > N) || (CAUSAL && key0 + kBC - 1 > qw0);
+  // MFMA phase, first half: O^T += V^T P^T for tile t (slots (kb, m) of P^T
+  // are accumulator rows 8m..8m+7). All operand reads are issued before the
+  // first product, so the LDS latency is paid once per half phase.
+  auto pv = [&](int t) {
+    const unsigned char* vs = smem + LY::kV + (t & 1) * LY::kTileBytes;
+    bf16x8 a[kKB][2][kDB];
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+          a[kb][m][db] = lds_tr_pair(vs + (kb * 32 + m * 16) * D * 2 + voff[db][0],
+                                     vs + (kb * 32 + m * 16) * D * 2 + voff[db][1]);
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        uint4 bu = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
+        const bf16x8 b = as_bf16x8(bu);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) oacc[db] = mfma32(a[kb][m][db], b, oacc[db]);
+      }
+#ifndef FA_EXP_NOSGB
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * kKB * kDB, 0);  // the LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kKB * kDB, 0);  // then the MFMAs
+#endif
+  };
+
+  // MFMA phase, second half: S^T = K Q^T for tile t
+  auto qk = [&](int t) {
+    const unsigned char* ks = smem + LY::kK + (t & 1) * LY::kTileBytes;
+    bf16x8 a[kDK][kKB];
+#pragma unroll
+    for (int kk = 0; kk < kDK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) a[kk][kb] = lds_ld16(ks + kb * 32 * D * 2 + koff[kk]);
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) s[kb] = zero16();
+#pragma unroll
+    for (int kk = 0; kk < kDK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) s[kb] = mfma32(a[kk][kb], qreg[kk], s[kb]);
+#ifndef FA_EXP_NOSGB
+    __builtin_amdgcn_sched_group_barrier(0x100, kDK * kKB, 0);  // the LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, kDK * kKB, 0);  // then the MFMAs
+#endif
+  };
+
+  // VALU phase: masks, online softmax and P for tile t
+  auto softmax = [&](int t) {
+    const int key0 = t * BC;
+    const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qw0);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
@@ -198,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         }
     }
 
-    // ---- row maximum over the tile (own 16*KB keys, then the other half)
+    // row maximum over the tile (own 16*KB keys, then the other half)
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -208,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     // c > 0, so a fully masked row gives cand = -inf and never grows m_run
     const float cand = mx * c;
 
-    // ---- move the reference maximum only when it is exceeded by the slack.
+    // move the reference maximum only when it is exceeded by the slack.
     // Every row sees key 0 in the first tile, so m_run is finite from then on
     // (on the first tile alpha = 2^-inf = 0 clears the empty accumulators).
     const bool grow = cand > m_run + kRescaleSlack;
@@ -223,9 +279,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       m_run = m_new;
     }
 
-    // ---- probabilities p = 2^(c*s - m) (masked scores: 2^-inf = 0), summed
-    // in fp32 (lse keeps fp32 accuracy) and packed to bf16 for P.V
-    uint32_t pk[kKB][8];
+    // probabilities p = 2^(c*s - m) (masked scores: 2^-inf = 0), summed in
+    // fp32 (lse keeps fp32 accuracy) and packed to bf16 for P.V
     float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
@@ -239,19 +294,70 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       }
     }
     l_run += ls0 + ls1;
+  };
 
-    // ---- O^T += V^T P^T; P^T slots (kb, m) are accumulator rows 8m..8m+7
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        uint4 bu = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
-        const bf16x8 b = as_bf16x8(bu);
-        const int chunk = 4 * kb + 2 * m + half;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db)
-          oacc[db] = mfma32(ld_tr<kBC>(sm.vt, db * 32 + col, chunk), b, oacc[db]);
+  // ---- phases. K_t is loaded in phase 2t-2 and read in phases 2t (leading
+  // group) and 2t+1 (following group); V_t is loaded in phase 2t and read in
+  // phases 2t+2 and 2t+3. Each stage is reloaded only after the barrier that
+  // ends its last read, and every wave waits for its own loads at the end of
+  // the phase before the one that first reads them.
+  auto mfma_phase = [&](int t) {
+    __builtin_amdgcn_s_setprio(1);
+    if (t >= 1 && t - 1 < wtiles) pv(t - 1);
+    // keep P (consumed above) and S (produced below) from being live at once
+    __builtin_amdgcn_sched_barrier(0);
+    if (t < wtiles) qk(t);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto fills = [&](int t) {  // at the start of phase 2t
+    if (t + 1 < ntiles) fill_tile(kg, t + 1, LY::kK, fk);
+    if (t < ntiles) fill_tile(vg, t, LY::kV, fv);
+  };
+
+  fill_tile(kg, 0, LY::kK, fk);
+  if constexpr (WAVES == kSequential) {
+    // K and V of tile t+1 load while tile t is computed: one barrier per
+    // tile, after which tile t is in LDS for every wave and every wave is
+    // done with tile t-1, whose stages the loads of tile t+1 overwrite
+    fill_tile(vg, 0, LY::kV, fv);
+    for (int t = 0; t < ntiles; ++t) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (t + 1 < ntiles) {
+        fill_tile(kg, t + 1, LY::kK, fk);
+        fill_tile(vg, t + 1, LY::kV, fv);
       }
+      if (t < wtiles) {
+        qk(t);
+        softmax(t);
+        pv(t);
+      }
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Each group has its own copy of the loop, so that only its own
+    // phase-crossing values (P for the leading group, S for the following
+    // one) stay live across iterations. Both copies pass the same barriers.
+    if (grp == 0) {
+      for (int t = 0; t <= ntiles; ++t) {
+        fills(t);
+        mfma_phase(t);                         // phase 2t:   X(t)
+        __syncthreads();
+        if (t < wtiles) softmax(t);            // phase 2t+1: V(t)
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    } else {
+      for (int t = 0; t <= ntiles; ++t) {
+        fills(t);
+        if (t >= 1 && t - 1 < wtiles) softmax(t - 1);  // phase 2t:   V(t-1)
+        __syncthreads();
+        mfma_phase(t);                                 // phase 2t+1: X(t)
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
   }
 
   // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2
@@ -280,6 +386,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   }
 }
 
+constexpr int kBC = 64;  // keys per tile
+#ifndef FA_EXP_SCHEDULE
+constexpr int kSchedule = kSequential;
+#else
+constexpr int kSchedule = FA_EXP_SCHEDULE;
+#endif
+
 template <int D, bool CAUSAL, typename TIn, typename TOut>
 hipError_t launch_typed(const FwdArgs& a) {
   FwdParams p;
@@ -290,14 +403,15 @@ hipError_t launch_typed(const FwdArgs& a) {
   p.lse = a.lse;
   p.BH = a.B * a.H;
   p.N = a.N;
-  p.nqb = (a.N + kBR - 1) / kBR;
+  p.nqb = (a.N + Shape<kSchedule>::kBR - 1) / Shape<kSchedule>::kBR;
   // c is kept positive: a zero or denormal scale is raised to 1e-30, which
   // changes no score by more than 1e-27 and keeps c * (-inf) = -inf
   p.c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   p.negate_q = a.scale < 0.0f;
   p.xcd_remap = (p.BH % 8) == 0;
   dim3 grid((unsigned)((long long)p.BH * p.nqb));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, TIn, TOut>), grid, dim3(kThreads), 0, a.stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, kBC, kSchedule, CAUSAL, TIn, TOut>), grid,
+                     dim3(Shape<kSchedule>::kThreads), 0, a.stream, p);
   return hipGetLastError();
 }
 
@@ -315,7 +429,7 @@ hipError_t launch_forward_bf16(const FwdArgs& a) { return launch_dtype<uint16_t,
 hipError_t launch_forward_f32(const FwdArgs& a) { return launch_dtype<float, float>(a); }
 
 long long forward_grid_size(int B, int H, int N) {
-  return (long long)B * H * ((N + kBR - 1) / kBR);
+  return (long long)B * H * ((N + Shape<kSchedule>::kBR - 1) / Shape<kSchedule>::kBR);
 }
 
 }  // namespace fa

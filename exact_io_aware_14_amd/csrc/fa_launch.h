@@ -29,7 +29,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* drow;  // workspace: D_i = sum_k dO_ik O_ik, [B,H,N] fp32
+  float* drow;  // workspace: D_i = sum_k dO_ik O_ik, then lse_i * log2(e); 2 x [B,H,N] fp32
   int B, H, N, d;
   float scale;
   int causal;
@@ -38,8 +38,8 @@ struct BwdArgs {
 
 hipError_t launch_forward_bf16(const FwdArgs& a);
 hipError_t launch_forward_f32(const FwdArgs& a);
-hipError_t launch_backward_prep(const BwdArgs& a);   // uses o, dout, drow
-hipError_t launch_backward_grads(const BwdArgs& a);  // uses everything but o
+hipError_t launch_backward_prep(const BwdArgs& a);   // uses o, dout, lse, drow
+hipError_t launch_backward_grads(const BwdArgs& a);  // uses q, k, v, dout, drow, outputs
 
 // Workgroups the forward launch uses (for grid-size validation).
 long long forward_grid_size(int B, int H, int N);

@@ -82,8 +82,9 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
                    hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_backward needs: B*H*N*sizeof(float), for the
- * row terms D_i = sum_k dO_ik O_ik. Returns 0 for empty or invalid shapes.
+ * Bytes of device workspace fa_backward needs: 2*B*H*N*sizeof(float), for
+ * the row terms D_i = sum_k dO_ik O_ik followed by lse_i * log2(e), each
+ * [B,H,N] fp32. Returns 0 for empty or invalid shapes.
  */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
 
@@ -101,7 +102,8 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d);
  *                      fp32 accumulation, rounded to nearest even once.
  *   workspace        : device buffer of at least
  *                      fa_backward_workspace_size(B,H,N,d) bytes, 16-byte
- *                      aligned; contents ignored on entry, holds D on return.
+ *                      aligned; contents ignored on entry, holds the row
+ *                      terms of fa_backward_prep on return.
  * Equivalent to fa_backward_prep followed by fa_backward_grads on the same
  * stream. Every output element is written by exactly one workgroup: dk and
  * dv by a pass over key blocks, dq by a pass over query-row blocks, with no
@@ -113,17 +115,19 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * First stage of fa_backward: D_i = sum_k dout_ik O_ik for every row, into
- * the workspace ([B,H,N] fp32). o and dout as for fa_backward. Errors as for
- * fa_backward (scale and causal are not arguments here).
+ * First stage of fa_backward: for every row, D_i = sum_k dout_ik O_ik and
+ * lse_i * log2(e), into the workspace (the first and second [B,H,N] fp32
+ * halves). o, dout and lse as for fa_backward. Errors as for fa_backward
+ * (scale and causal are not arguments here).
  */
-int fa_backward_prep(const void* o, const void* dout, int B, int H, int N, int d,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_backward_prep(const void* o, const void* dout, const float* lse, int B, int H, int N,
+                     int d, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Second stage of fa_backward: dq, dk, dv from q, k, v, dout, lse and the
- * row terms D that fa_backward_prep left in `workspace` (read only here).
- * Arguments, layouts and errors as for fa_backward.
+ * Second stage of fa_backward: dq, dk, dv from q, k, v, dout and the row
+ * terms fa_backward_prep left in `workspace` (read only here; lse enters
+ * through them). `lse` must still be a valid pointer. Arguments, layouts and
+ * errors as for fa_backward.
  */
 int fa_backward_grads(const void* q, const void* k, const void* v, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv,

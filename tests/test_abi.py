@@ -53,8 +53,8 @@ def test_strerror(lib):
 
 
 def test_workspace_size(lib):
-    assert fa.fa_backward_workspace_size(4, 16, 4096, 128) == 4 * 16 * 4096 * 4
-    assert fa.fa_backward_workspace_size(1, 1, 1, 64) == 4
+    assert fa.fa_backward_workspace_size(4, 16, 4096, 128) == 2 * 4 * 16 * 4096 * 4
+    assert fa.fa_backward_workspace_size(1, 1, 1, 64) == 8
     assert fa.fa_backward_workspace_size(0, 1, 1, 64) == 0
     assert fa.fa_backward_workspace_size(1, 1, 1, 96) == 0
     assert fa.fa_backward_workspace_size(1, 1, -5, 64) == 0
@@ -75,7 +75,7 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=64, scale=0.125, causa
 def bwd(lib, ws=P, ws_bytes=None, d=64, B=1, H=1, N=16, causal=0, scale=0.125, ptrs=None):
     ptrs = ptrs or [P] * 9
     if ws_bytes is None:
-        ws_bytes = B * H * N * 4 if min(B, H, N) > 0 else 0
+        ws_bytes = 2 * B * H * N * 4 if min(B, H, N) > 0 else 0
     return lib.fa_backward(*ptrs, B, H, N, d, scale, causal, ws, ws_bytes, NULL)
 
 
@@ -119,19 +119,20 @@ def test_backward_validation(lib):
         assert bwd(lib, ptrs=ptrs) == FA_ERR_ALIGN
     assert bwd(lib, ws=NULL) == FA_ERR_WORKSPACE
     assert bwd(lib, ws=PM) == FA_ERR_WORKSPACE
-    assert bwd(lib, ws_bytes=16 * 4 - 1) == FA_ERR_WORKSPACE
+    assert bwd(lib, ws_bytes=2 * 16 * 4 - 1) == FA_ERR_WORKSPACE
     assert bwd(lib, ptrs=[NULL] * 9, ws=NULL, N=0) == FA_OK
 
 
 def test_backward_stage_validation(lib):
-    ws = 16 * 4
-    assert lib.fa_backward_prep(P, P, 1, 1, 16, 80, P, ws, NULL) == FA_ERR_HEADDIM
-    assert lib.fa_backward_prep(P, P, 1, -1, 16, 64, P, ws, NULL) == FA_ERR_SHAPE
-    assert lib.fa_backward_prep(NULL, P, 1, 1, 16, 64, P, ws, NULL) == FA_ERR_NULL
-    assert lib.fa_backward_prep(P, PM, 1, 1, 16, 64, P, ws, NULL) == FA_ERR_ALIGN
-    assert lib.fa_backward_prep(P, P, 1, 1, 16, 64, P, ws - 4, NULL) == FA_ERR_WORKSPACE
-    assert lib.fa_backward_prep(P, P, 1, 1, 16, 64, NULL, ws, NULL) == FA_ERR_WORKSPACE
-    assert lib.fa_backward_prep(NULL, NULL, 1, 1, 0, 64, NULL, 0, NULL) == FA_OK
+    ws = 2 * 16 * 4
+    assert lib.fa_backward_prep(P, P, P, 1, 1, 16, 80, P, ws, NULL) == FA_ERR_HEADDIM
+    assert lib.fa_backward_prep(P, P, P, 1, -1, 16, 64, P, ws, NULL) == FA_ERR_SHAPE
+    assert lib.fa_backward_prep(NULL, P, P, 1, 1, 16, 64, P, ws, NULL) == FA_ERR_NULL
+    assert lib.fa_backward_prep(P, P, NULL, 1, 1, 16, 64, P, ws, NULL) == FA_ERR_NULL
+    assert lib.fa_backward_prep(P, PM, P, 1, 1, 16, 64, P, ws, NULL) == FA_ERR_ALIGN
+    assert lib.fa_backward_prep(P, P, P, 1, 1, 16, 64, P, ws - 4, NULL) == FA_ERR_WORKSPACE
+    assert lib.fa_backward_prep(P, P, P, 1, 1, 16, 64, NULL, ws, NULL) == FA_ERR_WORKSPACE
+    assert lib.fa_backward_prep(NULL, NULL, NULL, 1, 1, 0, 64, NULL, 0, NULL) == FA_OK
 
     def grads(ptrs=None, d=64, N=16, causal=0, scale=0.125, w=P, wb=ws):
         ptrs = ptrs or [P] * 8

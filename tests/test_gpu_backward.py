@@ -112,11 +112,13 @@ def test_backward_stages_match_backward():
         q, k, v, do = (x.to(DEV) for x in draw(shape, 44, with_grad=True))
         o, lse = fa_forward(q, k, v, causal=causal)
         ref = fa_backward(q, k, v, o, do, lse, causal=causal)
-        ws = fa_backward_prep(o, do)
-        # the row terms are D_i = sum_k dO_ik O_ik
-        drow = ws[: shape[0] * shape[1] * shape[2] * 4].view(torch.float32).view(shape[:3])
-        expect = (do.float() * o.float()).sum(-1)
-        assert torch.allclose(drow, expect, rtol=1e-5, atol=1e-5)
+        ws = fa_backward_prep(o, do, lse)
+        # the row terms are D_i = sum_k dO_ik O_ik, then lse_i * log2(e)
+        rows = shape[0] * shape[1] * shape[2]
+        terms = ws[: 2 * rows * 4].view(torch.float32)
+        expect = (do.float() * o.float()).sum(-1).reshape(-1)
+        assert torch.allclose(terms[:rows], expect, rtol=1e-5, atol=1e-5)
+        assert torch.allclose(terms[rows:], lse.reshape(-1) * 1.4426950408889634, rtol=1e-6)
         got = fa_backward_grads(q, k, v, do, lse, ws, causal=causal)
         torch.cuda.synchronize()
         for a, b in zip(ref, got):
