@@ -7,7 +7,7 @@
 //          dK/dV jobs, one per (batch, head, block of 128 keys), walk the
 //          query tiles and accumulate dV_j = sum_i P_ij dO_i and
 //          dK_j = scale * sum_i dS_ij Q_i for their own keys;
-//          dQ jobs, one per (batch, head, block of 128 query rows), walk the
+//          dQ jobs, one per (batch, head, block of 256 query rows), walk the
 //          key tiles and accumulate dQ_i = scale * sum_j dS_ij K_j
 //
 // with P_ij = exp(scale q_i.k_j - lse_i) recomputed from the forward pass's
@@ -21,13 +21,18 @@
 // section "より優れた並列処理". Every output element is written by exactly one
 // workgroup, so no atomics are needed and results are deterministic.
 //
+// Workgroups are 8 waves, two per SIMD, each under 256 registers.
 // MFMA formulations (32x32x16 bf16; layouts in fa_common.h):
-//   dK/dV job, lane = key:   S = Q K^T and dP = dO V^T with K^T, V^T held in
-//     registers as B operands and Q, dO rows read from LDS; dV^T += dO^T P
-//     and dK^T += Q^T dS with P, dS repacked in-lane as B operands and dO^T,
-//     Q^T read from the same row-major tiles through the transposing read.
-//   dQ job, lane = query:    S^T = K Q^T and dP^T = V dO^T with Q^T, dO^T in
-//     registers; dQ^T += K^T dS^T with K^T read through the transposing read.
+//   dK/dV job, lane = key: the workgroup's 128 keys of K and V stay in LDS;
+//     wave w owns keys 32*(w%4).. and rows 32*(w/4).. of every 64-row query
+//     tile. S = Q K^T and dP = dO V^T read both operands as LDS rows;
+//     dV^T += dO^T P and dK^T += Q^T dS take P, dS repacked in-lane as B
+//     operands and dO^T, Q^T from the row-major tiles through the
+//     transposing read. Waves w and w+4 add their partial dK, dV once, at
+//     the end, through LDS.
+//   dQ job, lane = query: 8 x 32 rows; S^T = K Q^T and dP^T = V dO^T with
+//     Q^T, dO^T in registers; dQ^T += K^T dS^T with K^T read through the
+//     transposing read.
 //
 // Tiles of 64 rows move global -> LDS with direct buffer loads (no
 // registers), double-buffered: tile t+1 loads while tile t is computed, one
@@ -40,10 +45,11 @@
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kBlock = 128;  // keys (dK/dV) or query rows (dQ) per workgroup
-constexpr int kTile = 64;    // rows of the streamed tile
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kKeyBlock = 128;  // keys per dK/dV job
+constexpr int kQBlock = 256;    // query rows per dQ job
+constexpr int kTile = 64;       // rows of a streamed tile
 
 struct BwdParams {
   const uint16_t* q;
@@ -57,7 +63,8 @@ struct BwdParams {
   uint16_t* dv;
   int BH;
   int N;
-  int nblk;         // 128-row blocks per head
+  int nkb;          // dK/dV jobs (128-key blocks) per head
+  int nqb;          // dQ jobs (256-row blocks) per head
   float c;          // scale * log2(e)
   float scale;
   int xcd_remap;
@@ -68,13 +75,15 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 
 // ---------------------------------------------------------------- prep
 
+constexpr int kPrepThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t* o,
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const uint16_t* o,
                                                             const uint16_t* dout,
                                                             const float* lse, float* drow,
                                                             float* lse2, long long rows) {
   constexpr int kLanesPerRow = D / 8;
-  constexpr int kRowsPerBlock = kThreads / kLanesPerRow;
+  constexpr int kRowsPerBlock = kPrepThreads / kLanesPerRow;
   const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
   const int ch = threadIdx.x % kLanesPerRow;
   float acc = 0.0f;
@@ -99,11 +108,12 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t* o,
 
 // ---------------------------------------------------------------- layout
 
-// Job of this workgroup in the grads launch. Every head owns 2*nblk jobs,
-// alternately dK/dV and dQ, each sequence ordered from the most expensive
-// block down (causal: dK/dV of the first key blocks, dQ of the last query
-// blocks). Consecutive workgroups go to the 8 XCDs in turn; when the head
-// count allows, each XCD gets whole heads so their K/V and Q/dO stay in its L2.
+// Job of this workgroup in the grads launch. Every head owns nkb dK/dV jobs
+// and nqb dQ jobs, taken alternately while both last, each sequence ordered
+// from the most expensive block down (causal: dK/dV of the first key
+// blocks, dQ of the last query blocks). Consecutive workgroups go to the 8
+// XCDs in turn; when the head count allows, each XCD gets whole heads so
+// their K/V and Q/dO stay in its L2.
 struct Job {
   int bh;
   int blk;
@@ -113,7 +123,7 @@ struct Job {
 template <bool CAUSAL>
 __device__ __forceinline__ Job job_of(const BwdParams& p) {
   const int L = blockIdx.x;
-  const int per_head = 2 * p.nblk;
+  const int per_head = p.nkb + p.nqb;
   int bh, j;
   if (p.xcd_remap) {
     const int xcd = L & 7, idx = L >> 3;
@@ -125,23 +135,43 @@ __device__ __forceinline__ Job job_of(const BwdParams& p) {
   }
   Job job;
   job.bh = bh;
-  job.is_dq = (j & 1) != 0;
-  const int rank = j >> 1;
-  job.blk = (CAUSAL && job.is_dq) ? (p.nblk - 1 - rank) : rank;
+  int rank;
+  if (j < 2 * p.nqb) {
+    job.is_dq = (j & 1) != 0;
+    rank = j >> 1;
+  } else {
+    job.is_dq = false;
+    rank = j - p.nqb;
+  }
+  job.blk = (CAUSAL && job.is_dq) ? (p.nqb - 1 - rank) : rank;
   return job;
 }
 
-// LDS of the grads launch (bytes). dK/dV jobs: Q and dO tiles plus the
-// tile's lse2 and D, two stages each; dQ jobs: K and V tiles, two stages.
+// LDS of the grads launch (bytes).
 template <int D>
 struct GLayout {
   static constexpr int kTileBytes = kTile * D * 2;
-  static constexpr int kA = 0;                    // Q (dK/dV) or K (dQ), stages 0, 1
-  static constexpr int kB = 2 * kTileBytes;       // dO (dK/dV) or V (dQ), stages 0, 1
-  static constexpr int kL = 4 * kTileBytes;       // lse2, stages 0, 1: 64 floats each
-  static constexpr int kR = kL + 2 * kTile * 4;   // D, stages 0, 1
-  static constexpr int kBytes = kR + 2 * kTile * 4;
-  static constexpr int kFill = kTileBytes / 1024 / kWaves;  // 1 KB blocks per wave and tile
+  static constexpr int kBlockBytes = kKeyBlock * D * 2;
+  // dK/dV job: the key block's K and V, then Q and dO tiles, lse2 and D of
+  // the tile, the tiles in two stages
+  static constexpr int kKb = 0;
+  static constexpr int kVb = kBlockBytes;
+  static constexpr int kQt = 2 * kBlockBytes;
+  static constexpr int kGt = kQt + 2 * kTileBytes;
+  static constexpr int kLv = kGt + 2 * kTileBytes;
+  static constexpr int kRv = kLv + 2 * kTile * 4;
+  static constexpr int kDkdvBytes = kRv + 2 * kTile * 4;
+  // dQ job: K and V tiles in two stages
+  static constexpr int kKt = 0;
+  static constexpr int kVt = 2 * kTileBytes;
+  static constexpr int kDqBytes = 4 * kTileBytes;
+  static constexpr int kBytes = kDkdvBytes > kDqBytes ? kDkdvBytes : kDqBytes;
+  // 1 KB blocks per wave to fill a tile / a key block
+  static constexpr int kFillTile = kTileBytes / 1024 / kWaves;
+  static constexpr int kFillBlock = kBlockBytes / 1024 / kWaves;
+  // partial dK, dV of the four waves w+4 (fp32), laid out [wave][dk|dv][db][r][lane]
+  static constexpr int kPartialBytes = 4 * 2 * (D / 32) * 16 * 64 * 4;
+  static_assert(kPartialBytes <= kDkdvBytes, "the partials reuse the job's LDS");
 };
 
 // Per-lane LDS offsets shared by both jobs.
@@ -149,7 +179,7 @@ template <int D>
 struct Offsets {
   uint32_t row[D / 16];       // MFMA operand rows: row col (+32 per block), chunk 2kk + half
   uint32_t tr[D / 32][2];     // transposing reads: d-block db, read 0/1 (+ 16-row bases)
-  uint32_t fill[GLayout<D>::kFill];
+  uint32_t ftile[GLayout<D>::kFillTile];
   __device__ __forceinline__ void init(int wave, int lane) {
     const int half = lane >> 5, col = lane & 31;
 #pragma unroll
@@ -159,17 +189,17 @@ struct Offsets {
 #pragma unroll
       for (int rd = 0; rd < 2; ++rd) tr[db][rd] = rows_t_offset<D>(db, rd, lane);
 #pragma unroll
-    for (int i = 0; i < GLayout<D>::kFill; ++i)
-      fill[i] = fill_lane_offset<D, kTile, kWaves>(i, wave, lane);
+    for (int i = 0; i < GLayout<D>::kFillTile; ++i)
+      ftile[i] = fill_lane_offset<D, kTile, kWaves>(i, wave, lane);
   }
 };
 
 // Start loading rows row0 .. row0+63 of a head-sized bf16 tensor into `dst`.
 template <int D>
-__device__ __forceinline__ void fill_rows(unsigned char* dst, const uint16_t* g, int row0, int N,
+__device__ __forceinline__ void fill_tile(unsigned char* dst, const uint16_t* g, int row0, int N,
                                           const Offsets<D>& off, int wave) {
   const auto r = make_rsrc(g + (size_t)row0 * D, (uint32_t)(N - row0) * D * 2u);
-  fill_direct<D, kTile, kWaves>(dst, r, off.fill, wave);
+  fill_direct<D, kTile, kWaves>(dst, r, off.ftile, wave);
 }
 
 // Start loading 64 floats v[row0 .. row0+63] (zeros past N) into `dst`.
@@ -177,6 +207,21 @@ __device__ __forceinline__ void fill_vec(unsigned char* dst, const float* g, int
                                          int lane) {
   const auto r = make_rsrc(g + row0, (uint32_t)(N - row0) * 4u);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)dst, 4, (uint32_t)lane * 4u, 0, 0, 0);
+}
+
+// 32x32 outputs of this lane (column c, 4 groups of 4 rows) as bf16 rows:
+// element r of block db is d = 32*db + 8*(r/4) + 4*half + (r%4).
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16* acc, float sc, int half) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = db * 32 + 8 * g4 + 4 * half;
+      const uint2 w = {pack_bf16x2(acc[db][4 * g4] * sc, acc[db][4 * g4 + 1] * sc),
+                       pack_bf16x2(acc[db][4 * g4 + 2] * sc, acc[db][4 * g4 + 3] * sc)};
+      *reinterpret_cast<uint2*>(dst + d0) = w;
+    }
 }
 
 // ---------------------------------------------------------------- dK / dV
@@ -190,6 +235,8 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3;   // key sub-block of this wave
+  const int qh = wave >> 2;  // which 32 rows of each query tile
   const int half = lane >> 5, col = lane & 31;
   const int N = p.N;
   const size_t head = (size_t)bh * N;
@@ -198,25 +245,24 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   const float* lg = p.lse2 + head;
   const float* rg = p.drow + head;
 
-  const int k0 = kblk * kBlock;
-  const int kw0 = k0 + wave * 32;  // this wave's first key
+  const int k0 = kblk * kKeyBlock;
+  const int kw0 = k0 + 32 * kw;  // this wave's first key
   const int mykey = kw0 + col;
 
   Offsets<D> off;
   off.init(wave, lane);
 
-  // K^T and V^T columns of this lane's key, as B operands (zeros past N)
-  bf16x8 kreg[kDK], vreg[kDK];
+  // the workgroup's keys of K and V (zeros past N), for the whole job
   {
-    const uint32_t bytes = (uint32_t)N * D * 2u;
-    const auto kr = make_rsrc(p.k + head * D, bytes);
-    const auto vr = make_rsrc(p.v + head * D, bytes);
+    const uint32_t bytes = (uint32_t)(N - k0) * D * 2u;
+    const auto kr = make_rsrc(p.k + (head + k0) * D, bytes);
+    const auto vr = make_rsrc(p.v + (head + k0) * D, bytes);
+    uint32_t fb[LY::kFillBlock];
 #pragma unroll
-    for (int kk = 0; kk < kDK; ++kk) {
-      const uint32_t e = (uint32_t)(mykey * D + kk * 16 + half * 8);
-      kreg[kk] = as_bf16x8(load8<uint16_t>(kr, e));
-      vreg[kk] = as_bf16x8(load8<uint16_t>(vr, e));
-    }
+    for (int i = 0; i < LY::kFillBlock; ++i)
+      fb[i] = fill_lane_offset<D, kKeyBlock, kWaves>(i, wave, lane);
+    fill_direct<D, kKeyBlock, kWaves>(smem + LY::kKb, kr, fb, wave);
+    fill_direct<D, kKeyBlock, kWaves>(smem + LY::kVb, vr, fb, wave);
   }
   f32x16 dvacc[kDB], dkacc[kDB];
 #pragma unroll
@@ -228,117 +274,122 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   const int ntiles = (N + kTile - 1) / kTile;
   const int t0 = CAUSAL ? k0 / kTile : 0;  // earlier query rows see none of these keys
   const float c = p.c;
+  const unsigned char* kb = smem + LY::kKb + kw * 32 * D * 2;  // this wave's key rows
+  const unsigned char* vb = smem + LY::kVb + kw * 32 * D * 2;
 
   auto fill = [&](int t) {
     const int st = t & 1, r0 = t * kTile;
-    fill_rows<D>(smem + LY::kA + st * LY::kTileBytes, qg, r0, N, off, wave);
-    fill_rows<D>(smem + LY::kB + st * LY::kTileBytes, gg, r0, N, off, wave);
-    if (wave == 0) fill_vec(smem + LY::kL + st * kTile * 4, lg, r0, N, lane);
-    if (wave == 1) fill_vec(smem + LY::kR + st * kTile * 4, rg, r0, N, lane);
+    fill_tile<D>(smem + LY::kQt + st * LY::kTileBytes, qg, r0, N, off, wave);
+    fill_tile<D>(smem + LY::kGt + st * LY::kTileBytes, gg, r0, N, off, wave);
+    if (wave == 0) fill_vec(smem + LY::kLv + st * kTile * 4, lg, r0, N, lane);
+    if (wave == 1) fill_vec(smem + LY::kRv + st * kTile * 4, rg, r0, N, lane);
   };
 
   if (t0 < ntiles) fill(t0);
   for (int t = t0; t < ntiles; ++t) {
-    // tile t is in LDS for every wave, and every wave is done with tile t-1,
-    // whose stage the loads of tile t+1 overwrite
+    // tile t (and, first time round, the key block) is in LDS for every
+    // wave, and every wave is done with tile t-1, whose stage the loads of
+    // tile t+1 overwrite
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t + 1 < ntiles) fill(t + 1);
 
-    const int qs = t * kTile;
-    if (CAUSAL && qs + kTile - 1 < kw0) continue;  // every row of the tile precedes our keys
-    const bool need_mask = CAUSAL && qs < kw0 + 31;
+    const int r0 = t * kTile + 32 * qh;  // this wave's first query row
+    if (CAUSAL && r0 + 31 < kw0) continue;  // every row precedes every key: P = 0
+    const bool need_mask = CAUSAL && r0 < kw0 + 31;
     const int st = t & 1;
-    const unsigned char* qt = smem + LY::kA + st * LY::kTileBytes;
-    const unsigned char* gt = smem + LY::kB + st * LY::kTileBytes;
-    const float* l2t = reinterpret_cast<const float*>(smem + LY::kL + st * kTile * 4);
-    const float* drt = reinterpret_cast<const float*>(smem + LY::kR + st * kTile * 4);
+    const unsigned char* qt = smem + LY::kQt + st * LY::kTileBytes + qh * 32 * D * 2;
+    const unsigned char* gt = smem + LY::kGt + st * LY::kTileBytes + qh * 32 * D * 2;
+    const float* l2t = reinterpret_cast<const float*>(smem + LY::kLv + st * kTile * 4) + 32 * qh;
+    const float* drt = reinterpret_cast<const float*>(smem + LY::kRv + st * kTile * 4) + 32 * qh;
 
-    // ---- S = Q K^T and dP = dO V^T: rows = the tile's queries, column = key
-    uint32_t pk[2][8], dsk[2][8];
+    // ---- S = Q K^T and dP = dO V^T: rows = the wave's 32 queries, column = key
+    f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      bf16x8 qa[kDK], ga[kDK];
+    for (int k2 = 0; k2 < kDK; k2 += 2) {
+      bf16x8 qa[2], ga[2], ka[2], va[2];
 #pragma unroll
-      for (int kk = 0; kk < kDK; ++kk) {
-        qa[kk] = lds_ld16(qt + qb * 32 * D * 2 + off.row[kk]);
-        ga[kk] = lds_ld16(gt + qb * 32 * D * 2 + off.row[kk]);
-      }
-      f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int kk = 0; kk < kDK; ++kk) {
-        s = mfma32(qa[kk], kreg[kk], s);
-        dp = mfma32(ga[kk], vreg[kk], dp);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDK, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kDK, 0);
-
-      // ---- P = 2^(c*S - lse2) and dS = P * (dP - D), packed to bf16
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int r0 = qb * 32 + 8 * g4 + 4 * half;  // tile rows of elements 4g4..4g4+3
-        const f32x4 l2v = *reinterpret_cast<const f32x4*>(&l2t[r0]);
-        const f32x4 drv = *reinterpret_cast<const f32x4*>(&drt[r0]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g4 + i;
-          float pr = fast_exp2(__builtin_fmaf(s[r], c, -l2v[i]));
-          if (need_mask) pr = (qs + r0 + i < mykey) ? 0.0f : pr;
-          pv[r] = pr;
-          dsv[r] = pr * (dp[r] - drv[i]);
-        }
+      for (int u = 0; u < 2; ++u) {
+        qa[u] = lds_ld16(qt + off.row[k2 + u]);
+        ga[u] = lds_ld16(gt + off.row[k2 + u]);
+        ka[u] = lds_ld16(kb + off.row[k2 + u]);
+        va[u] = lds_ld16(vb + off.row[k2 + u]);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pk[qb][j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
-        dsk[qb][j] = pack_bf16x2(dsv[2 * j], dsv[2 * j + 1]);
+      for (int u = 0; u < 2; ++u) {
+        s = mfma32(qa[u], ka[u], s);
+        dp = mfma32(ga[u], va[u], dp);
       }
     }
 
-    // ---- dV^T += dO^T P and dK^T += Q^T dS; slots (qb, m) are accumulator
-    // rows 8m..8m+7 of S, i.e. tile rows 32qb + 16m + ...
+    // ---- P = 2^(c*S - lse2) and dS = P * (dP - D), packed to bf16
+    uint32_t pk[8], dsk[8];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int rr = 8 * g4 + 4 * half;  // rows of elements 4g4..4g4+3 (within the 32)
+      const f32x4 l2v = *reinterpret_cast<const f32x4*>(&l2t[rr]);
+      const f32x4 drv = *reinterpret_cast<const f32x4*>(&drt[rr]);
+      float pv[4], dsv[4];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int rb = (qb * 32 + m * 16) * D * 2;
-        bf16x8 ga[kDB], qa[kDB];
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          ga[db] = lds_tr_pair(gt + rb + off.tr[db][0], gt + rb + off.tr[db][1]);
-          qa[db] = lds_tr_pair(qt + rb + off.tr[db][0], qt + rb + off.tr[db][1]);
-        }
-        const uint4 pu = {pk[qb][4 * m], pk[qb][4 * m + 1], pk[qb][4 * m + 2], pk[qb][4 * m + 3]};
-        const uint4 du = {dsk[qb][4 * m], dsk[qb][4 * m + 1], dsk[qb][4 * m + 2],
-                          dsk[qb][4 * m + 3]};
-        const bf16x8 pb = as_bf16x8(pu), db8 = as_bf16x8(du);
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          dvacc[db] = mfma32(ga[db], pb, dvacc[db]);
-          dkacc[db] = mfma32(qa[db], db8, dkacc[db]);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * kDB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kDB, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i;
+        float pr = fast_exp2(__builtin_fmaf(s[r], c, -l2v[i]));
+        if (need_mask) pr = (r0 + rr + i < mykey) ? 0.0f : pr;
+        pv[i] = pr;
+        dsv[i] = pr * (dp[r] - drv[i]);
       }
+      pk[2 * g4] = pack_bf16x2(pv[0], pv[1]);
+      pk[2 * g4 + 1] = pack_bf16x2(pv[2], pv[3]);
+      dsk[2 * g4] = pack_bf16x2(dsv[0], dsv[1]);
+      dsk[2 * g4 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+    }
+
+    // ---- dV^T += dO^T P and dK^T += Q^T dS; slots m are accumulator rows
+    // 8m..8m+7 of S, i.e. the wave's rows 16m + ...
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int rb = m * 16 * D * 2;
+      bf16x8 gta[kDB], qta[kDB];
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        gta[db] = lds_tr_pair(gt + rb + off.tr[db][0], gt + rb + off.tr[db][1]);
+        qta[db] = lds_tr_pair(qt + rb + off.tr[db][0], qt + rb + off.tr[db][1]);
+      }
+      const uint4 pu = {pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]};
+      const uint4 du = {dsk[4 * m], dsk[4 * m + 1], dsk[4 * m + 2], dsk[4 * m + 3]};
+      const bf16x8 pb = as_bf16x8(pu), db8 = as_bf16x8(du);
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        dvacc[db] = mfma32(gta[db], pb, dvacc[db]);
+        dkacc[db] = mfma32(qta[db], db8, dkacc[db]);
+      }
+    }
   }
 
-  if (mykey < N) {
-    uint16_t* dkg = p.dk + (head + mykey) * D;
-    uint16_t* dvg = p.dv + (head + mykey) * D;
-    const float sc = p.scale;
+  // ---- waves w+4 hand their partial sums to waves w through LDS
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // every wave is done with the tiles
+  float* part = reinterpret_cast<float*>(smem) + kw * 2 * kDB * 16 * 64;
+  if (qh == 1) {
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * half;
-        const uint2 wk = {pack_bf16x2(dkacc[db][4 * g4] * sc, dkacc[db][4 * g4 + 1] * sc),
-                          pack_bf16x2(dkacc[db][4 * g4 + 2] * sc, dkacc[db][4 * g4 + 3] * sc)};
-        const uint2 wv = {pack_bf16x2(dvacc[db][4 * g4], dvacc[db][4 * g4 + 1]),
-                          pack_bf16x2(dvacc[db][4 * g4 + 2], dvacc[db][4 * g4 + 3])};
-        *reinterpret_cast<uint2*>(dkg + d0) = wk;
-        *reinterpret_cast<uint2*>(dvg + d0) = wv;
+      for (int r = 0; r < 16; ++r) {
+        part[((0 * kDB + db) * 16 + r) * 64 + lane] = dkacc[db][r];
+        part[((1 * kDB + db) * 16 + r) * 64 + lane] = dvacc[db][r];
       }
+  }
+  __syncthreads();
+  if (qh == 0 && mykey < N) {
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dkacc[db][r] += part[((0 * kDB + db) * 16 + r) * 64 + lane];
+        dvacc[db][r] += part[((1 * kDB + db) * 16 + r) * 64 + lane];
+      }
+    store_rows<D>(p.dk + (head + mykey) * D, dkacc, p.scale, half);
+    store_rows<D>(p.dv + (head + mykey) * D, dvacc, 1.0f, half);
   }
 }
 
@@ -359,7 +410,7 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   const uint16_t* kg = p.k + head * D;
   const uint16_t* vg = p.v + head * D;
 
-  const int q0 = qblk * kBlock;
+  const int q0 = qblk * kQBlock;
   const int qw0 = q0 + wave * 32;
   const int myq = qw0 + col;
   const int wave_last = min(qw0 + 32, N) - 1;
@@ -389,13 +440,15 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   for (int i = 0; i < kDB; ++i) dqacc[i] = zero16();
 
   const int ntiles_all = (N + kTile - 1) / kTile;
-  const int ntiles = CAUSAL ? min(ntiles_all, (min(q0 + kBlock, N) - 1) / kTile + 1) : ntiles_all;
+  const int ntiles =
+      CAUSAL ? min(ntiles_all, (min(q0 + kQBlock, N) - 1) / kTile + 1) : ntiles_all;
+  const int wtiles = qw0 >= N ? 0 : (CAUSAL ? wave_last / kTile + 1 : ntiles_all);
   const float c = p.c;
 
   auto fill = [&](int t) {
     const int st = t & 1, r0 = t * kTile;
-    fill_rows<D>(smem + LY::kA + st * LY::kTileBytes, kg, r0, N, off, wave);
-    fill_rows<D>(smem + LY::kB + st * LY::kTileBytes, vg, r0, N, off, wave);
+    fill_tile<D>(smem + LY::kKt + st * LY::kTileBytes, kg, r0, N, off, wave);
+    fill_tile<D>(smem + LY::kVt + st * LY::kTileBytes, vg, r0, N, off, wave);
   };
 
   fill(0);
@@ -403,31 +456,32 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t + 1 < ntiles) fill(t + 1);
+    if (t >= wtiles) continue;  // no visible key for this wave
 
     const int key0 = t * kTile;
-    if (CAUSAL && key0 > wave_last) continue;
     const bool need_mask = CAUSAL && key0 + kTile - 1 > qw0;
     const int st = t & 1;
-    const unsigned char* kt = smem + LY::kA + st * LY::kTileBytes;
-    const unsigned char* vt = smem + LY::kB + st * LY::kTileBytes;
+    const unsigned char* kt = smem + LY::kKt + st * LY::kTileBytes;
+    const unsigned char* vt = smem + LY::kVt + st * LY::kTileBytes;
 
     uint32_t dsk[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 ka[kDK], va[kDK];
-#pragma unroll
-      for (int kk = 0; kk < kDK; ++kk) {
-        ka[kk] = lds_ld16(kt + kb * 32 * D * 2 + off.row[kk]);
-        va[kk] = lds_ld16(vt + kb * 32 * D * 2 + off.row[kk]);
-      }
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int kk = 0; kk < kDK; ++kk) {
-        s = mfma32(ka[kk], qreg[kk], s);
-        dp = mfma32(va[kk], greg[kk], dp);
+      for (int k4 = 0; k4 < kDK; k4 += 4) {
+        bf16x8 ka[4], va[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ka[u] = lds_ld16(kt + kb * 32 * D * 2 + off.row[k4 + u]);
+          va[u] = lds_ld16(vt + kb * 32 * D * 2 + off.row[k4 + u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          s = mfma32(ka[u], qreg[k4 + u], s);
+          dp = mfma32(va[u], greg[k4 + u], dp);
+        }
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDK, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kDK, 0);
       float dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -457,28 +511,14 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
         const bf16x8 b = as_bf16x8(du);
 #pragma unroll
         for (int db = 0; db < kDB; ++db) dqacc[db] = mfma32(ka[db], b, dqacc[db]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, kDB, 0);
       }
   }
 
-  if (myq < N) {
-    uint16_t* dqg = p.dq + (head + myq) * D;
-    const float sc = p.scale;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * half;
-        const uint2 w = {pack_bf16x2(dqacc[db][4 * g4] * sc, dqacc[db][4 * g4 + 1] * sc),
-                         pack_bf16x2(dqacc[db][4 * g4 + 2] * sc, dqacc[db][4 * g4 + 3] * sc)};
-        *reinterpret_cast<uint2*>(dqg + d0) = w;
-      }
-  }
+  if (myq < N) store_rows<D>(p.dq + (head + myq) * D, dqacc, p.scale, half);
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_grads_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[GLayout<D>::kBytes];
   const Job job = job_of<CAUSAL>(p);
   if (job.is_dq)
@@ -501,7 +541,8 @@ BwdParams make_params(const BwdArgs& a) {
   p.dv = static_cast<uint16_t*>(a.dv);
   p.BH = a.B * a.H;
   p.N = a.N;
-  p.nblk = (a.N + kBlock - 1) / kBlock;
+  p.nkb = (a.N + kKeyBlock - 1) / kKeyBlock;
+  p.nqb = (a.N + kQBlock - 1) / kQBlock;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
   p.xcd_remap = (p.BH % 8) == 0;
@@ -511,9 +552,9 @@ BwdParams make_params(const BwdArgs& a) {
 template <int D>
 hipError_t launch_prep_typed(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.H * a.N;
-  constexpr int kRowsPerBlock = kThreads / (D / 8);
+  constexpr int kRowsPerBlock = kPrepThreads / (D / 8);
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), grid, dim3(kThreads), 0, a.stream,
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), grid, dim3(kPrepThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
                      a.lse, a.drow, a.drow + rows, rows);
   return hipGetLastError();
@@ -522,7 +563,7 @@ hipError_t launch_prep_typed(const BwdArgs& a) {
 template <int D, bool CAUSAL>
 hipError_t launch_grads_typed(const BwdArgs& a) {
   const BwdParams p = make_params<D>(a);
-  const dim3 grid((unsigned)(2LL * p.BH * p.nblk));
+  const dim3 grid((unsigned)((long long)p.BH * (p.nkb + p.nqb)));
   hipLaunchKernelGGL((bwd_grads_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
 }
@@ -542,7 +583,8 @@ hipError_t launch_backward_grads(const BwdArgs& a) {
 long long backward_grid_size(int B, int H, int N) {
   const long long rows = (long long)B * H * N;
   const long long row_blocks = (rows + 15) / 16;
-  const long long blocks = 2LL * B * H * ((N + kBlock - 1) / kBlock);
+  const long long blocks = (long long)B * H *
+                           ((N + kKeyBlock - 1) / kKeyBlock + (N + kQBlock - 1) / kQBlock);
   return row_blocks > blocks ? row_blocks : blocks;
 }
 
