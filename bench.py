@@ -16,7 +16,10 @@ forward alone on the same input. `roofline` describes the dominant kernel
 timed on a bounded sample of the same workload on this host.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-       python bench.py --copy-calibration   (a plain 1 GiB copy, for counters)
+                       [--copy-calibration]
+--copy-calibration first runs a plain device copy of 1 GiB (torch's copy
+kernel), whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic
+counters of the attention kernels in the same profiled run.
 """
 
 from __future__ import annotations
@@ -96,14 +99,14 @@ def cpu_baseline(w, heads: int):
 
 
 def copy_calibration():
-    """A plain device copy of 1 GiB, for scaling the FETCH_SIZE/WRITE_SIZE counters."""
+    """A plain device copy of 1 GiB (read 1 GiB, write 1 GiB), run once."""
     import torch
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4}))
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def main():
@@ -122,7 +125,6 @@ def main():
                  "(attention heads would shard across GPUs with no exchange)")
     if args.copy_calibration:
         copy_calibration()
-        return
 
     import torch
 
