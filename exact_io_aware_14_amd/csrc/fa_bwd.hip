@@ -39,6 +39,8 @@
 // barrier per tile. Rows past the end of a sequence load as zeros, so they
 // add nothing to any gradient (their Q, dO, K and V are zero); only the
 // causal mask needs explicit handling, on diagonal tiles.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -285,23 +287,16 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
     if (wave == 1) fill_vec(smem + LY::kRv + st * kTile * 4, rg, r0, N, lane);
   };
 
-  if (t0 < ntiles) fill(t0);
-  for (int t = t0; t < ntiles; ++t) {
-    // tile t (and, first time round, the key block) is in LDS for every
-    // wave, and every wave is done with tile t-1, whose stage the loads of
-    // tile t+1 overwrite
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 1 < ntiles) fill(t + 1);
-
+  // one query tile; MASK: the tile crosses the causal diagonal of this
+  // wave's keys; ST: its LDS stage (t - t0 is even for stage 0)
+  auto tile = [&](int t, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const int ST = t & 1;
     const int r0 = t * kTile + 32 * qh;  // this wave's first query row
-    if (CAUSAL && r0 + 31 < kw0) continue;  // every row precedes every key: P = 0
-    const bool need_mask = CAUSAL && r0 < kw0 + 31;
-    const int st = t & 1;
-    const unsigned char* qt = smem + LY::kQt + st * LY::kTileBytes + qh * 32 * D * 2;
-    const unsigned char* gt = smem + LY::kGt + st * LY::kTileBytes + qh * 32 * D * 2;
-    const float* l2t = reinterpret_cast<const float*>(smem + LY::kLv + st * kTile * 4) + 32 * qh;
-    const float* drt = reinterpret_cast<const float*>(smem + LY::kRv + st * kTile * 4) + 32 * qh;
+    const unsigned char* qt = smem + LY::kQt + ST * LY::kTileBytes + qh * 32 * D * 2;
+    const unsigned char* gt = smem + LY::kGt + ST * LY::kTileBytes + qh * 32 * D * 2;
+    const float* l2t = reinterpret_cast<const float*>(smem + LY::kLv + ST * kTile * 4) + 32 * qh;
+    const float* drt = reinterpret_cast<const float*>(smem + LY::kRv + ST * kTile * 4) + 32 * qh;
 
     // ---- S = Q K^T and dP = dO V^T: rows = the wave's 32 queries, column = key
     f32x16 s = zero16(), dp = zero16();
@@ -334,7 +329,7 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g4 + i;
         float pr = fast_exp2(__builtin_fmaf(s[r], c, -l2v[i]));
-        if (need_mask) pr = (r0 + rr + i < mykey) ? 0.0f : pr;
+        if constexpr (MASK) pr = (r0 + rr + i < mykey) ? 0.0f : pr;
         pv[i] = pr;
         dsv[i] = pr * (dp[r] - drv[i]);
       }
@@ -364,6 +359,35 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
         dkacc[db] = mfma32(qta[db], db8, dkacc[db]);
       }
     }
+  };
+
+  // tile t (and, the first time, the key block) is in LDS for every wave,
+  // and every wave is done with tile t-1, whose stage the loads of tile t+1
+  // overwrite
+  // tile t (and, the first time, the key block) is in LDS for every wave,
+  // and every wave is done with tile t-1, whose stage the loads of tile t+1
+  // overwrite
+  auto sync_fill = [&](int t) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < ntiles) fill(t + 1);
+  };
+  // Causal: this wave's rows r0 .. r0+31 of tile t see all of its keys once
+  // r0 >= kw0 + 31; before that the tile crosses the diagonal (masked), and
+  // with r0 + 31 < kw0 it sees none. Each wave walks its masked tiles and
+  // its unmasked tiles in two loops (every iteration passes one barrier),
+  // so no loop holds both versions of the tile body.
+  // first tile that needs no mask (none needs one without the causal mask)
+  const int tm =
+      CAUSAL ? min(ntiles, max(t0, (kw0 + 31 - 32 * qh + kTile - 1) / kTile)) : t0;
+  if (t0 < ntiles) fill(t0);
+  for (int t = t0; t < tm; ++t) {
+    sync_fill(t);
+    if (t * kTile + 32 * qh + 31 >= kw0) tile(t, std::true_type());
+  }
+  for (int t = tm; t < ntiles; ++t) {
+    sync_fill(t);
+    tile(t, std::false_type());
   }
 
   // ---- waves w+4 hand their partial sums to waves w through LDS
@@ -451,18 +475,13 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
     fill_tile<D>(smem + LY::kVt + st * LY::kTileBytes, vg, r0, N, off, wave);
   };
 
-  fill(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 1 < ntiles) fill(t + 1);
-    if (t >= wtiles) continue;  // no visible key for this wave
-
+  // one key tile; MASK: it crosses the causal diagonal of this wave's rows
+  auto tile = [&](int t, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const int ST = t & 1;
     const int key0 = t * kTile;
-    const bool need_mask = CAUSAL && key0 + kTile - 1 > qw0;
-    const int st = t & 1;
-    const unsigned char* kt = smem + LY::kKt + st * LY::kTileBytes;
-    const unsigned char* vt = smem + LY::kVt + st * LY::kTileBytes;
+    const unsigned char* kt = smem + LY::kKt + ST * LY::kTileBytes;
+    const unsigned char* vt = smem + LY::kVt + ST * LY::kTileBytes;
 
     uint32_t dsk[2][8];
 #pragma unroll
@@ -486,7 +505,7 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pr = fast_exp2(__builtin_fmaf(s[r], c, -l2));
-        if (need_mask) {
+        if constexpr (MASK) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
           pr = key <= myq ? pr : 0.0f;
         }
@@ -512,6 +531,26 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
 #pragma unroll
         for (int db = 0; db < kDB; ++db) dqacc[db] = mfma32(ka[db], b, dqacc[db]);
       }
+  };
+
+  auto sync_fill = [&](int t) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < ntiles) fill(t + 1);
+  };
+  // Causal: key tile t is unmasked for all of this wave's rows while
+  // t*64 + 63 <= qw0, crosses the diagonal up to tile wtiles-1, and is
+  // invisible after. Unmasked and masked tiles run in two loops (every
+  // iteration passes one barrier), so no loop holds both tile bodies.
+  const int tm = CAUSAL ? min(wtiles, max(0, (qw0 + 1) / kTile)) : wtiles;
+  fill(0);
+  for (int t = 0; t < tm; ++t) {
+    sync_fill(t);
+    tile(t, std::false_type());
+  }
+  for (int t = tm; t < ntiles; ++t) {
+    sync_fill(t);
+    if (t < wtiles) tile(t, std::true_type());
   }
 
   if (myq < N) store_rows<D>(p.dq + (head + myq) * D, dqacc, p.scale, half);
