@@ -364,9 +364,6 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   // tile t (and, the first time, the key block) is in LDS for every wave,
   // and every wave is done with tile t-1, whose stage the loads of tile t+1
   // overwrite
-  // tile t (and, the first time, the key block) is in LDS for every wave,
-  // and every wave is done with tile t-1, whose stage the loads of tile t+1
-  // overwrite
   auto sync_fill = [&](int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
