@@ -2,8 +2,8 @@
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.
 """
-from .attention import (backward, backward_head, forward, forward_head, merge,
+from .attention import (backward, backward_head, forward, forward_head, kv_head, merge,
                         probabilities_head)
 
-__all__ = ["forward", "forward_head", "backward", "backward_head", "merge",
+__all__ = ["forward", "forward_head", "backward", "backward_head", "kv_head", "merge",
            "probabilities_head"]

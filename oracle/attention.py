@@ -28,6 +28,12 @@ What it computes (per batch b and head h, all heads independent):
   definition above: with P the softmax, D_i = sum_k dO_ik O_ik,
   dP = dO V^T, dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q,
   dV = P^T dO.
+* Grouped-query and multi-query attention (nearauto.com page, section
+  "新機能"): several query heads share one K/V head. ``forward`` and
+  ``backward`` take K and V with Hkv heads, Hkv dividing H; query head h
+  reads K/V head h // (H / Hkv) (consecutive groups: the page does not say
+  which heads form a set), and a shared K/V head's gradient is the sum over
+  its query heads.
 * ``merge`` combines the results over two disjoint key sets; the unite.ai
   page's formula 2 ("Unione della Softmax") is garbled as printed, and the
   reading used is the plain one: rescale each part's unnormalised sums by
@@ -138,28 +144,50 @@ def backward_head(q, k, v, do, scale, causal):
     return dq, dk, dv
 
 
+def kv_head(h, heads, kv_heads):
+    """K/V head read by query head h when `heads` query heads share
+    `kv_heads` K/V heads (grouped-query attention; kv_heads = 1 is
+    multi-query attention, kv_heads = heads ordinary multi-head attention).
+
+    The nearauto.com page, section "新機能", says each set of query heads
+    shares one K/V head. It does not say which heads form a set; the reading
+    used is consecutive groups of heads // kv_heads query heads."""
+    if kv_heads < 1 or heads % kv_heads != 0:
+        raise ValueError(f"{heads} query heads cannot share {kv_heads} K/V heads evenly")
+    return h // (heads // kv_heads)
+
+
 def forward(q, k, v, scale, causal):
-    """Batched forward over [B, H, N, d] float64 arrays -> (O, lse[B, H, N])."""
+    """Batched forward: q [B, H, N, d], k and v [B, Hkv, N, d] float64 with
+    Hkv dividing H (Hkv = H: multi-head) -> (O [B, H, N, d], lse [B, H, N]).
+    Query head h attends over K/V head kv_head(h, H, Hkv)."""
     q = np.asarray(q, dtype=np.float64)
     bsz, heads, n, d = q.shape
+    kv_heads = np.shape(k)[1]
     out = np.zeros((bsz, heads, n, v.shape[-1]), dtype=np.float64)
     lse = np.zeros((bsz, heads, n), dtype=np.float64)
     for b in range(bsz):
         for h in range(heads):
-            out[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], scale, causal)
+            g = kv_head(h, heads, kv_heads)
+            out[b, h], lse[b, h] = forward_head(q[b, h], k[b, g], v[b, g], scale, causal)
     return out, lse
 
 
 def backward(q, k, v, do, scale, causal):
-    """Batched backward over [B, H, N, d] float64 arrays -> (dQ, dK, dV)."""
+    """Batched backward over the shapes of ``forward`` -> (dQ, dK, dV). A K/V
+    head read by several query heads receives the sum of their gradients (the
+    chain rule for a shared input)."""
     q = np.asarray(q, dtype=np.float64)
+    heads, kv_heads = q.shape[1], np.shape(k)[1]
     dq = np.zeros_like(q)
     dk = np.zeros(np.shape(k), dtype=np.float64)
     dv = np.zeros(np.shape(v), dtype=np.float64)
     for b in range(q.shape[0]):
-        for h in range(q.shape[1]):
-            dq[b, h], dk[b, h], dv[b, h] = backward_head(
-                q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+        for h in range(heads):
+            g = kv_head(h, heads, kv_heads)
+            dq[b, h], dk_h, dv_h = backward_head(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+            dk[b, g] += dk_h
+            dv[b, g] += dv_h
     return dq, dk, dv
 
 

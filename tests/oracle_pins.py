@@ -288,6 +288,73 @@ def pin_backward_invariants():
         _close((do * o).sum(axis=1), (p * (do @ v.T)).sum(axis=1), 1e-11, "D identity")
 
 
+# ---------------------------------------------------------------- grouped K/V heads
+
+GQA_SHAPES = ((1, 4, 2, 5, 3), (2, 6, 3, 4, 2), (1, 3, 1, 6, 4), (1, 2, 2, 3, 2))
+
+
+def _torch_gqa(q, k, v, do, scale, causal):
+    """torch fp64 autograd with each K/V head copied to its query heads by
+    repeat_interleave (consecutive groups); autograd sums the copies'
+    gradients."""
+    heads, kv_heads = q.shape[1], k.shape[1]
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    ke = tk.repeat_interleave(heads // kv_heads, dim=1)
+    ve = tv.repeat_interleave(heads // kv_heads, dim=1)
+    s = torch.matmul(tq, ke.transpose(-1, -2)) * scale
+    if causal:
+        n = s.shape[-1]
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), -math.inf)
+    o = torch.matmul(torch.softmax(s, dim=-1), ve)
+    (o * torch.tensor(do, dtype=torch.float64)).sum().backward()
+    return o.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def pin_gqa_vs_autograd():
+    rng = np.random.default_rng(21)
+    for bsz, heads, kv_heads, n, d in GQA_SHAPES:
+        for causal in (False, True):
+            q = rng.standard_normal((bsz, heads, n, d))
+            k = rng.standard_normal((bsz, kv_heads, n, d))
+            v = rng.standard_normal((bsz, kv_heads, n, d))
+            do = rng.standard_normal((bsz, heads, n, d))
+            o, _ = A.forward(q, k, v, 0.6, causal)
+            grads = A.backward(q, k, v, do, 0.6, causal)
+            ref = _torch_gqa(q, k, v, do, 0.6, causal)
+            what = f"H={heads} Hkv={kv_heads} causal={causal}"
+            _close(o, ref[0], 1e-12, f"grouped O vs torch {what}")
+            for name, mine, r in zip(("dQ", "dK", "dV"), grads, ref[1:]):
+                _close(mine, r, 1e-11, f"grouped {name} vs autograd {what}")
+
+
+def pin_gqa_finite_differences():
+    rng = np.random.default_rng(22)
+    eps = 1e-6
+    for heads, kv_heads, causal in ((4, 2, True), (3, 1, False)):
+        n, d, scale = 3, 2, 0.9
+        q = rng.standard_normal((1, heads, n, d))
+        k = rng.standard_normal((1, kv_heads, n, d))
+        v = rng.standard_normal((1, kv_heads, n, d))
+        do = rng.standard_normal((1, heads, n, d))
+        grads = A.backward(q, k, v, do, scale, causal)
+
+        def loss(qq, kk, vv):
+            return float(np.sum(do * A.forward(qq, kk, vv, scale, causal)[0]))
+
+        for which in (1, 2):  # the shared K and V
+            base = [q, k, v]
+            num = np.zeros_like(base[which])
+            for idx in np.ndindex(*num.shape):
+                plus = [x.copy() for x in base]
+                minus = [x.copy() for x in base]
+                plus[which][idx] += eps
+                minus[which][idx] -= eps
+                num[idx] = (loss(*plus) - loss(*minus)) / (2 * eps)
+            _close(grads[which], num, 1e-7,
+                   f"grouped finite differences input {which} H={heads} Hkv={kv_heads}")
+
+
 ALL_PINS = [pin_golden_forward, pin_golden_backward, pin_vs_torch_sdpa,
             pin_backward_vs_autograd, pin_finite_differences, pin_brute_force,
-            pin_online_recurrence, pin_forward_invariants, pin_backward_invariants]
+            pin_online_recurrence, pin_forward_invariants, pin_backward_invariants,
+            pin_gqa_vs_autograd, pin_gqa_finite_differences]

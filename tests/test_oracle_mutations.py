@@ -74,6 +74,27 @@ def _fwd_transposed_p(q, k, v, scale, causal, rows=None):
     return o[ids], lse
 
 
+def _kv_head_modulo(h, heads, kv_heads):
+    return h % kv_heads
+
+
+def _kv_head_reversed(h, heads, kv_heads):
+    return (heads - 1 - h) // (heads // kv_heads)
+
+
+def _backward_not_summed(q, k, v, do, scale, causal):
+    heads, kv_heads = q.shape[1], k.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros(np.shape(k))
+    dv = np.zeros(np.shape(v))
+    for b in range(q.shape[0]):
+        for h in range(heads):
+            g = A.kv_head(h, heads, kv_heads)
+            dq[b, h], dk[b, g], dv[b, g] = A.backward_head(q[b, h], k[b, g], v[b, g], do[b, h],
+                                                        scale, causal)
+    return dq, dk, dv
+
+
 MUTATIONS = {
     "scale_dropped": ("_scores", _scores_no_scale),
     "causal_mask_flipped": ("_scores", _scores_flipped_mask),
@@ -87,6 +108,9 @@ MUTATIONS = {
     "bwd_dv_untransposed": ("backward_head", _bwd_variant("dv_no_transpose")),
     "bwd_dq_scale_dropped": ("backward_head", _bwd_variant("dq_no_scale")),
     "fwd_p_transposed": ("forward_head", _fwd_transposed_p),
+    "gqa_head_map_modulo": ("kv_head", _kv_head_modulo),
+    "gqa_head_map_reversed": ("kv_head", _kv_head_reversed),
+    "gqa_grads_overwritten": ("backward", _backward_not_summed),
 }
 
 
@@ -94,7 +118,7 @@ MUTATIONS = {
 def test_mutation_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     A._ORIG = {a: getattr(A, a) for a in ("_scores", "_row_softmax_stats", "forward_head",
-                                          "backward_head")}
+                                          "backward_head", "backward", "kv_head")}
     monkeypatch.setattr(A, attr, fn)
     failed = []
     for pin in ALL_PINS:
