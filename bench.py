@@ -15,8 +15,13 @@ forward alone on the same input. `roofline` describes the dominant kernel
 (the one with the longest launches), `cpu_baseline` the fp64 CPU oracle
 timed on a bounded sample of the same workload on this host.
 
+A second object, `gqa`, times the same step on the grouped-query workload
+B=4, H=32 query heads sharing H_kv=8 K/V heads, N=4096, d=128, causal (seed
+6), through fa_forward_gqa, fa_backward_prep and fa_backward_grads_gqa; its
+FLOP count is that of 32 heads.
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-                       [--copy-calibration]
+                       [--copy-calibration] [--no-gqa] [--gqa-only]
 --copy-calibration first runs a plain device copy of 1 GiB (torch's copy
 kernel), whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic
 counters of the attention kernels in the same profiled run.
@@ -37,6 +42,7 @@ sys.path.insert(0, ROOT)
 # MI355X dense bf16 MFMA peak: 256 CUs x 4 SIMDs x 1024 flop/clk x 2.4 GHz.
 PEAK_BF16_TFLOPS = 2516.6
 WORKLOAD = "fwdbwd_causal_b4h16n4096d128"
+GQA_WORKLOAD = "fwdbwd_causal_gqa_b4h32kv8n4096d128"
 METRIC = "attention TFLOP/s (fwd, fwd+bwd) bf16 on 1 MI355X; % of MFMA peak"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["exact_io_aware_14_amd/csrc/fa_common.h", "exact_io_aware_14_amd/csrc/fa_fwd.hip",
@@ -56,16 +62,17 @@ def counted_flops(w):
     return fwd, 2.5 * fwd
 
 
-def measured_traffic(kernel: str, src_hash: str):
-    """HBM bytes per launch from the committed counter runs, if they were
-    taken on the kernel sources as they are now; else None."""
+def measured_traffic(kernel: str, src_hash: str, workload: str = WORKLOAD):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter runs, if they were taken on the kernel sources as they are now;
+    else None."""
     try:
         data = json.load(open(PROFILE_TRAFFIC))
     except (OSError, ValueError):
         return None
     if data.get("source_hash") != src_hash:
         return None
-    entry = data.get("kernels", {}).get(kernel)
+    entry = data.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
     return None if entry is None else entry.get("bytes_per_launch")
 
 
@@ -98,6 +105,61 @@ def cpu_baseline(w, heads: int):
                       f"in fp64 numpy, {dt:.1f} s; the rate extrapolates linearly to all heads"}
 
 
+def time_steps(step, steps, warmup, stream):
+    """Run `step(ev)` warmup + steps times; returns the mean ms of each of the
+    three launches of a step (HIP events on `stream`) and of the whole step."""
+    import torch
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    parts = [sum(e[j].elapsed_time(e[j + 1]) for e in events) / steps for j in range(3)]
+    return parts, sum(e[0].elapsed_time(e[3]) for e in events) / steps
+
+
+def measure_gqa(steps, warmup):
+    import torch
+
+    from exact_io_aware_14_amd import (fa_backward_grads_gqa, fa_backward_prep,
+                                       fa_backward_workspace_size, fa_forward_gqa)
+    from exact_io_aware_14_amd.inputs import by_name, draw
+
+    w = by_name(GQA_WORKLOAD)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x.to(dev) for x in draw(w.shape, w.seed, with_grad=True, kv_heads=w.kv_heads))
+    o = torch.empty_like(q)
+    lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa_backward_workspace_size(*w.shape), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        fa_forward_gqa(q, k, v, w.scale, w.causal, o, lse, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa_backward_prep(o, do, lse, ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fa_backward_grads_gqa(q, k, v, do, lse, ws, w.scale, w.causal, dq, dk, dv, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    (fwd_ms, prep_ms, grads_ms), step_ms = time_steps(step, steps, warmup, stream)
+    fwd_f, bwd_f = counted_flops(w)
+    return {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d,
+            "causal": w.causal, "steps": steps,
+            "fwdbwd_tflops": round((fwd_f + bwd_f) / (step_ms * 1e-3) / 1e12, 2),
+            "fwd_tflops": round(fwd_f / (fwd_ms * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(bwd_f / ((prep_ms + grads_ms) * 1e-3) / 1e12, 2),
+            "ms": {"fwd": round(fwd_ms, 4), "bwd_prep": round(prep_ms, 4),
+                   "bwd_grads": round(grads_ms, 4)}}
+
+
 def copy_calibration():
     """A plain device copy of 1 GiB (read 1 GiB, write 1 GiB), run once."""
     import torch
@@ -117,6 +179,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true")
+    ap.add_argument("--gqa-only", action="store_true",
+                    help="time only the grouped-query step (for its profile)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -125,6 +190,9 @@ def main():
                  "(attention heads would shard across GPUs with no exchange)")
     if args.copy_calibration:
         copy_calibration()
+    if args.gqa_only:
+        print(json.dumps({"gqa": measure_gqa(args.steps, args.warmup)}), flush=True)
+        return
 
     import torch
 
@@ -217,6 +285,8 @@ def main():
         "kernel_source_hash": src_hash,
         "roofline": roofline,
     }
+    if not args.no_gqa:
+        out["gqa"] = measure_gqa(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
     print(json.dumps(out), flush=True)

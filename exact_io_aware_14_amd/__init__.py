@@ -13,9 +13,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["FAError", "fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_prep",
-           "fa_backward_grads", "fa_backward_workspace_size", "fa_strerror", "library",
-           "LIB_PATH"]
+__all__ = ["FAError", "fa_forward", "fa_forward_gqa", "fa_forward_f32", "fa_backward",
+           "fa_backward_gqa", "fa_backward_prep", "fa_backward_grads", "fa_backward_grads_gqa",
+           "fa_backward_workspace_size", "fa_strerror", "library", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -41,6 +41,15 @@ def library():
         lib.fa_forward.restype = i
         lib.fa_forward_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_forward_f32.restype = i
+        for name, argtypes in (
+                ("fa_forward_gqa", [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]),
+                ("fa_backward_gqa", [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
+                                     vp, sz, vp]),
+                ("fa_backward_grads_gqa", [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
+                                           vp, sz, vp])):
+            if hasattr(lib, name):  # an older build without them fails when they are called
+                getattr(lib, name).argtypes = argtypes
+                getattr(lib, name).restype = i
         lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
         lib.fa_backward_workspace_size.restype = sz
         lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
@@ -92,14 +101,22 @@ def _check(t, name, dtype, shape, device):
         raise ValueError(f"{name} must be on {device} (a HIP device)")
 
 
-def _forward(fn_name, q, k, v, scale, causal, o, lse, stream, dtype):
+def _kv_heads(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d] and [B, H_kv, N, d]")
+    return k.shape[1]
+
+
+def _forward(fn_name, q, k, v, scale, causal, o, lse, stream, dtype, gqa=False):
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
+    Hkv = _kv_heads(q, k) if gqa else H
     dev = q.device
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check(t, name, dtype, (B, H, N, d), dev)
+    _check(q, "q", dtype, (B, H, N, d), dev)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, dtype, (B, Hkv, N, d), dev)
     if o is None:
         o = torch.empty((B, H, N, d), dtype=dtype, device=dev)
     if lse is None:
@@ -108,8 +125,9 @@ def _forward(fn_name, q, k, v, scale, causal, o, lse, stream, dtype):
     _check(lse, "lse", torch.float32, (B, H, N), dev)
     if scale is None:
         scale = d ** -0.5
+    heads = (B, H, Hkv) if gqa else (B, H)
     st = getattr(library(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                     B, H, N, d, float(scale), int(bool(causal)),
+                                     *heads, N, d, float(scale), int(bool(causal)),
                                      _stream(stream))
     if st != 0:
         raise FAError(st, fn_name)
@@ -122,26 +140,40 @@ def fa_forward(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None)
                     _torch().bfloat16)
 
 
+def fa_forward_gqa(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None):
+    """Grouped-query forward: q [B,H,N,d], k and v [B,H_kv,N,d] bf16 with H_kv
+    dividing H (see fa_forward_gqa in fa.h)."""
+    return _forward("fa_forward_gqa", q, k, v, scale, causal, o, lse, stream,
+                    _torch().bfloat16, gqa=True)
+
+
 def fa_forward_f32(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None):
     """fp32 in/out variant: inputs are rounded to bf16 as they are loaded."""
     return _forward("fa_forward_f32", q, k, v, scale, causal, o, lse, stream,
                     _torch().float32)
 
 
-def _bwd_check(q, tensors, lse, outs):
+def _bwd_check(q, tensors, lse, outs, Hkv=None):
+    """Checks [B,H,N,d] query-side tensors and [B,Hkv,N,d] K/V-side tensors
+    (names k, v, dk, dv); allocates missing outputs."""
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
+    Hkv = H if Hkv is None else Hkv
     dev = q.device
+
+    def shape_of(name):
+        return (B, Hkv, N, d) if name in ("k", "v", "dk", "dv") else (B, H, N, d)
+
     for name, t in tensors:
-        _check(t, name, torch.bfloat16, (B, H, N, d), dev)
+        _check(t, name, torch.bfloat16, shape_of(name), dev)
     if lse is not None:
         _check(lse, "lse", torch.float32, (B, H, N), dev)
     res = []
     for name, t in outs:
-        t = torch.empty_like(q) if t is None else t
-        _check(t, name, torch.bfloat16, (B, H, N, d), dev)
+        t = torch.empty(shape_of(name), dtype=torch.bfloat16, device=dev) if t is None else t
+        _check(t, name, torch.bfloat16, shape_of(name), dev)
         res.append(t)
     return (B, H, N, d), dev, res
 
@@ -199,4 +231,44 @@ def fa_backward_grads(q, k, v, dout, lse, workspace, scale=None, causal=False, d
                                      _stream(stream))
     if st != 0:
         raise FAError(st, "fa_backward_grads")
+    return dq, dk, dv
+
+
+def fa_backward_gqa(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
+                    workspace=None, stream=None):
+    """Grouped-query backward: dq [B,H,N,d]; dk, dv [B,H_kv,N,d], each the sum
+    over its query heads (see fa_backward_gqa in fa.h)."""
+    Hkv = _kv_heads(q, k)
+    shape, dev, (dq, dk, dv) = _bwd_check(
+        q, (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)), lse,
+        (("dq", dq), ("dk", dk), ("dv", dv)), Hkv)
+    ws, ws_bytes = _workspace(shape, dev, workspace)
+    B, H, N, d = shape
+    scale = d ** -0.5 if scale is None else scale
+    st = library().fa_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
+                                   int(bool(causal)), _ptr(ws), ws_bytes, _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_backward_gqa")
+    return dq, dk, dv
+
+
+def fa_backward_grads_gqa(q, k, v, dout, lse, workspace, scale=None, causal=False, dq=None,
+                          dk=None, dv=None, stream=None):
+    """Second backward stage for grouped-query attention (see fa.h)."""
+    Hkv = _kv_heads(q, k)
+    shape, dev, (dq, dk, dv) = _bwd_check(
+        q, (("q", q), ("k", k), ("v", v), ("dout", dout)), lse,
+        (("dq", dq), ("dk", dk), ("dv", dv)), Hkv)
+    if workspace is None or workspace.device != dev:
+        raise ValueError("workspace from fa_backward_prep is required, on the same device")
+    B, H, N, d = shape
+    scale = d ** -0.5 if scale is None else scale
+    st = library().fa_backward_grads_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                         _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d,
+                                         float(scale), int(bool(causal)), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_backward_grads_gqa")
     return dq, dk, dv

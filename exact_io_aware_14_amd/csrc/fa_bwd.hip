@@ -63,10 +63,11 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  int BH;
+  int BH;           // batch * query heads
+  int group;        // query heads per K/V head (1: multi-head attention)
   int N;
-  int nkb;          // dK/dV jobs (128-key blocks) per head
-  int nqb;          // dQ jobs (256-row blocks) per head
+  int nkb;          // dK/dV jobs (128-key blocks) per K/V head
+  int nqb;          // dQ jobs (256-row blocks) per query head
   float c;          // scale * log2(e)
   float scale;
   int xcd_remap;
@@ -110,14 +111,15 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const uint16_t* 
 
 // ---------------------------------------------------------------- layout
 
-// Job of this workgroup in the grads launch. Every head owns nkb dK/dV jobs
-// and nqb dQ jobs, taken alternately while both last, each sequence ordered
-// from the most expensive block down (causal: dK/dV of the first key
-// blocks, dQ of the last query blocks). Consecutive workgroups go to the 8
-// XCDs in turn; when the head count allows, each XCD gets whole heads so
-// their K/V and Q/dO stay in its L2.
+// Job of this workgroup in the grads launch. Every K/V head owns nkb dK/dV
+// jobs and group * nqb dQ jobs (those of its query heads). The two kinds
+// are taken alternately while both last, each sequence ordered from the
+// most expensive block down (causal: dK/dV of the first key blocks, dQ of
+// the last query blocks). Consecutive workgroups go to the 8 XCDs in turn;
+// when the head count allows, each XCD gets whole K/V heads (with their
+// query heads) so that their K/V and Q/dO stay in its L2.
 struct Job {
-  int bh;
+  int bh;    // dK/dV: the K/V head (batch * K/V heads); dQ: the query head
   int blk;
   bool is_dq;
 };
@@ -125,27 +127,38 @@ struct Job {
 template <bool CAUSAL>
 __device__ __forceinline__ Job job_of(const BwdParams& p) {
   const int L = blockIdx.x;
-  const int per_head = p.nkb + p.nqb;
-  int bh, j;
+  const int ndq = p.group * p.nqb;
+  const int per_head = p.nkb + ndq;
+  const int bhkv = p.BH / p.group;
+  int kvh, j;
   if (p.xcd_remap) {
     const int xcd = L & 7, idx = L >> 3;
-    bh = (idx / per_head) * 8 + xcd;
+    kvh = (idx / per_head) * 8 + xcd;
     j = idx % per_head;
   } else {
-    bh = L % p.BH;
-    j = L / p.BH;
+    kvh = L % bhkv;
+    j = L / bhkv;
   }
+  const int both = p.nkb < ndq ? p.nkb : ndq;
   Job job;
-  job.bh = bh;
   int rank;
-  if (j < 2 * p.nqb) {
+  if (j < 2 * both) {
     job.is_dq = (j & 1) != 0;
     rank = j >> 1;
   } else {
-    job.is_dq = false;
-    rank = j - p.nqb;
+    job.is_dq = ndq > p.nkb;
+    rank = j - both;
   }
-  job.blk = (CAUSAL && job.is_dq) ? (p.nqb - 1 - rank) : rank;
+  if (job.is_dq) {
+    // rank r: query block r / group (from the last one under the causal
+    // mask) of query head r % group of this K/V head
+    const int qbr = rank / p.group;
+    job.bh = kvh * p.group + rank % p.group;
+    job.blk = CAUSAL ? (p.nqb - 1 - qbr) : qbr;
+  } else {
+    job.bh = kvh;
+    job.blk = rank;
+  }
   return job;
 }
 
@@ -241,11 +254,9 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   const int qh = wave >> 2;  // which 32 rows of each query tile
   const int half = lane >> 5, col = lane & 31;
   const int N = p.N;
-  const size_t head = (size_t)bh * N;
-  const uint16_t* qg = p.q + head * D;
-  const uint16_t* gg = p.dout + head * D;
-  const float* lg = p.lse2 + head;
-  const float* rg = p.drow + head;
+  const size_t head = (size_t)bh * N;  // bh: the K/V head
+  // its query heads are bh*group .. bh*group+group-1
+  const size_t qhead0 = (size_t)bh * p.group * N;
 
   const int k0 = kblk * kKeyBlock;
   const int kw0 = k0 + 32 * kw;  // this wave's first key
@@ -279,19 +290,20 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   const unsigned char* kb = smem + LY::kKb + kw * 32 * D * 2;  // this wave's key rows
   const unsigned char* vb = smem + LY::kVb + kw * 32 * D * 2;
 
-  auto fill = [&](int t) {
-    const int st = t & 1, r0 = t * kTile;
-    fill_tile<D>(smem + LY::kQt + st * LY::kTileBytes, qg, r0, N, off, wave);
-    fill_tile<D>(smem + LY::kGt + st * LY::kTileBytes, gg, r0, N, off, wave);
-    if (wave == 0) fill_vec(smem + LY::kLv + st * kTile * 4, lg, r0, N, lane);
-    if (wave == 1) fill_vec(smem + LY::kRv + st * kTile * 4, rg, r0, N, lane);
+  // load tile t of query head jq of the group into LDS stage st
+  auto fill = [&](int jq, int t, int st) {
+    const size_t qh = qhead0 + (size_t)jq * N;
+    const int r0 = t * kTile;
+    fill_tile<D>(smem + LY::kQt + st * LY::kTileBytes, p.q + qh * D, r0, N, off, wave);
+    fill_tile<D>(smem + LY::kGt + st * LY::kTileBytes, p.dout + qh * D, r0, N, off, wave);
+    if (wave == 0) fill_vec(smem + LY::kLv + st * kTile * 4, p.lse2 + qh, r0, N, lane);
+    if (wave == 1) fill_vec(smem + LY::kRv + st * kTile * 4, p.drow + qh, r0, N, lane);
   };
 
-  // one query tile; MASK: the tile crosses the causal diagonal of this
-  // wave's keys; ST: its LDS stage (t - t0 is even for stage 0)
-  auto tile = [&](int t, auto mask_c) {
+  // one query tile t, in LDS stage ST; MASK: the tile crosses the causal
+  // diagonal of this wave's keys
+  auto tile = [&](int t, int ST, auto mask_c) {
     constexpr bool MASK = decltype(mask_c)::value;
-    const int ST = t & 1;
     const int r0 = t * kTile + 32 * qh;  // this wave's first query row
     const unsigned char* qt = smem + LY::kQt + ST * LY::kTileBytes + qh * 32 * D * 2;
     const unsigned char* gt = smem + LY::kGt + ST * LY::kTileBytes + qh * 32 * D * 2;
@@ -361,13 +373,19 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
     }
   };
 
-  // tile t (and, the first time, the key block) is in LDS for every wave,
-  // and every wave is done with tile t-1, whose stage the loads of tile t+1
-  // overwrite
-  auto sync_fill = [&](int t) {
+  // The group's query heads one after another, each over tiles t0 ..
+  // ntiles-1; `step` counts the tiles walked and picks the LDS stage. At
+  // each step, the tile (and, the first time, the key block) is in LDS for
+  // every wave, and every wave is done with the previous step, whose stage
+  // the loads of the next step overwrite.
+  int step = 0;
+  auto sync_fill = [&](int jq, int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) fill(t + 1);
+    if (t + 1 < ntiles)
+      fill(jq, t + 1, (step + 1) & 1);
+    else if (jq + 1 < p.group)
+      fill(jq + 1, t0, (step + 1) & 1);
   };
   // Causal: this wave's rows r0 .. r0+31 of tile t see all of its keys once
   // r0 >= kw0 + 31; before that the tile crosses the diagonal (masked), and
@@ -377,14 +395,16 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   // first tile that needs no mask (none needs one without the causal mask)
   const int tm =
       CAUSAL ? min(ntiles, max(t0, (kw0 + 31 - 32 * qh + kTile - 1) / kTile)) : t0;
-  if (t0 < ntiles) fill(t0);
-  for (int t = t0; t < tm; ++t) {
-    sync_fill(t);
-    if (t * kTile + 32 * qh + 31 >= kw0) tile(t, std::true_type());
-  }
-  for (int t = tm; t < ntiles; ++t) {
-    sync_fill(t);
-    tile(t, std::false_type());
+  if (t0 < ntiles) fill(0, t0, 0);
+  for (int jq = 0; jq < p.group; ++jq) {
+    for (int t = t0; t < tm; ++t, ++step) {
+      sync_fill(jq, t);
+      if (t * kTile + 32 * qh + 31 >= kw0) tile(t, step & 1, std::true_type());
+    }
+    for (int t = tm; t < ntiles; ++t, ++step) {
+      sync_fill(jq, t);
+      tile(t, step & 1, std::false_type());
+    }
   }
 
   // ---- waves w+4 hand their partial sums to waves w through LDS
@@ -427,9 +447,10 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int N = p.N;
-  const size_t head = (size_t)bh * N;
-  const uint16_t* kg = p.k + head * D;
-  const uint16_t* vg = p.v + head * D;
+  const size_t head = (size_t)bh * N;  // bh: the query head
+  const size_t kvhead = (size_t)(bh / p.group) * N;
+  const uint16_t* kg = p.k + kvhead * D;
+  const uint16_t* vg = p.v + kvhead * D;
 
   const int q0 = qblk * kQBlock;
   const int qw0 = q0 + wave * 32;
@@ -576,12 +597,13 @@ BwdParams make_params(const BwdArgs& a) {
   p.dk = static_cast<uint16_t*>(a.dk);
   p.dv = static_cast<uint16_t*>(a.dv);
   p.BH = a.B * a.H;
+  p.group = a.H / a.Hkv;
   p.N = a.N;
   p.nkb = (a.N + kKeyBlock - 1) / kKeyBlock;
   p.nqb = (a.N + kQBlock - 1) / kQBlock;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
-  p.xcd_remap = (p.BH % 8) == 0;
+  p.xcd_remap = (p.BH / p.group) % 8 == 0;
   return p;
 }
 
@@ -599,7 +621,7 @@ hipError_t launch_prep_typed(const BwdArgs& a) {
 template <int D, bool CAUSAL>
 hipError_t launch_grads_typed(const BwdArgs& a) {
   const BwdParams p = make_params<D>(a);
-  const dim3 grid((unsigned)((long long)p.BH * (p.nkb + p.nqb)));
+  const dim3 grid((unsigned)((long long)(p.BH / p.group) * (p.nkb + p.group * p.nqb)));
   hipLaunchKernelGGL((bwd_grads_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
 }
@@ -616,11 +638,11 @@ hipError_t launch_backward_grads(const BwdArgs& a) {
   return a.causal ? launch_grads_typed<128, true>(a) : launch_grads_typed<128, false>(a);
 }
 
-long long backward_grid_size(int B, int H, int N) {
+long long backward_grid_size(int B, int H, int Hkv, int N) {
   const long long rows = (long long)B * H * N;
   const long long row_blocks = (rows + 15) / 16;
-  const long long blocks = (long long)B * H *
-                           ((N + kKeyBlock - 1) / kKeyBlock + (N + kQBlock - 1) / kQBlock);
+  const long long blocks = (long long)B * Hkv * ((N + kKeyBlock - 1) / kKeyBlock) +
+                           (long long)B * H * ((N + kQBlock - 1) / kQBlock);
   return row_blocks > blocks ? row_blocks : blocks;
 }
 

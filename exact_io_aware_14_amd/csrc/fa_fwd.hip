@@ -58,12 +58,14 @@ struct FwdParams {
   const void* v;
   void* o;
   float* lse;
-  int BH;        // batch * heads
+  int BH;        // batch * query heads
+  int H;         // query heads
+  int group;     // query heads per K/V head (1: multi-head attention)
   int N;         // sequence length
   int nqb;       // query blocks per head
   float c;       // |scale| * log2(e), at least 1e-30
   int negate_q;  // scale < 0: Q is negated on load and |scale| is used
-  int xcd_remap; // heads grouped per XCD (requires BH % 8 == 0)
+  int xcd_remap; // K/V heads grouped per XCD (requires BH / group % 8 == 0)
 };
 
 template <int D, int BC, int WAVES>
@@ -116,9 +118,11 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
   const int L = blockIdx.x;
   if (p.xcd_remap) {
     // consecutive workgroups go to the 8 XCDs in turn; give each XCD whole
-    // heads so the K/V of a head is re-read from that XCD's L2
-    int xcd = L & 7, idx = L >> 3;
-    bh = (idx / p.nqb) * 8 + xcd;
+    // K/V heads (with all query heads that read them) so the K/V of a head
+    // is re-read from that XCD's L2. Query head bh reads K/V head
+    // bh / group: the query heads of K/V head kv are kv*group .. +group-1.
+    const int xcd = L & 7, idx = L >> 3, slot = idx / p.nqb;
+    bh = ((slot / p.group) * 8 + xcd) * p.group + slot % p.group;
     qbr = idx % p.nqb;
   } else {
     bh = L % p.BH;
@@ -128,9 +132,10 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
   const int qb = CAUSAL ? (p.nqb - 1 - qbr) : qbr;
   const int N = p.N;
   const size_t head_off = (size_t)bh * (size_t)N * D;
+  const size_t kv_off = (size_t)(bh / p.group) * (size_t)N * D;
   const TIn* qg = reinterpret_cast<const TIn*>(p.q) + head_off;
-  const TIn* kg = reinterpret_cast<const TIn*>(p.k) + head_off;
-  const TIn* vg = reinterpret_cast<const TIn*>(p.v) + head_off;
+  const TIn* kg = reinterpret_cast<const TIn*>(p.k) + kv_off;
+  const TIn* vg = reinterpret_cast<const TIn*>(p.v) + kv_off;
 
   const int q0 = qb * kBR;                                        // first row of the block
   const int qw0 = q0 + grp * kRowsPerGroup + (wave & 3) * kRowsPerWave;  // this wave's
@@ -402,13 +407,15 @@ hipError_t launch_typed(const FwdArgs& a) {
   p.o = a.o;
   p.lse = a.lse;
   p.BH = a.B * a.H;
+  p.H = a.H;
+  p.group = a.H / a.Hkv;
   p.N = a.N;
   p.nqb = (a.N + Shape<kSchedule>::kBR - 1) / Shape<kSchedule>::kBR;
   // c is kept positive: a zero or denormal scale is raised to 1e-30, which
   // changes no score by more than 1e-27 and keeps c * (-inf) = -inf
   p.c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   p.negate_q = a.scale < 0.0f;
-  p.xcd_remap = (p.BH % 8) == 0;
+  p.xcd_remap = (p.BH / p.group) % 8 == 0;
   dim3 grid((unsigned)((long long)p.BH * p.nqb));
   hipLaunchKernelGGL((fwd_kernel<D, kBC, kSchedule, CAUSAL, TIn, TOut>), grid,
                      dim3(Shape<kSchedule>::kThreads), 0, a.stream, p);

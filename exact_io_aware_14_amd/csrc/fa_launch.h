@@ -17,6 +17,7 @@ struct FwdArgs {
   float scale;
   int causal;
   hipStream_t stream;
+  int Hkv;  // K/V heads; divides H (H: multi-head attention)
 };
 
 struct BwdArgs {
@@ -34,6 +35,7 @@ struct BwdArgs {
   float scale;
   int causal;
   hipStream_t stream;
+  int Hkv;  // K/V heads of k, v, dk, dv; divides H (H: multi-head attention)
 };
 
 hipError_t launch_forward_bf16(const FwdArgs& a);
@@ -43,6 +45,6 @@ hipError_t launch_backward_grads(const BwdArgs& a);  // uses q, k, v, dout, drow
 
 // Workgroups the forward launch uses (for grid-size validation).
 long long forward_grid_size(int B, int H, int N);
-long long backward_grid_size(int B, int H, int N);
+long long backward_grid_size(int B, int H, int Hkv, int N);
 
 }  // namespace fa

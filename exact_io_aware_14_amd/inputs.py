@@ -8,7 +8,8 @@ Recipe: config k seeds ``torch.Generator('cpu').manual_seed(k)`` and draws, in
 this order, Q, K, V (then dO for a backward workload) with ``torch.randn`` in
 float32, i.i.d. N(0, 1); bf16 workloads round these draws to bf16 (round to
 nearest even) on the CPU. The oracle receives the same rounded values upcast
-exactly to float64.
+exactly to float64. With grouped K/V heads (Hkv < H), K and V are drawn with
+Hkv heads and Q, dO with H.
 """
 
 from __future__ import annotations
@@ -30,10 +31,15 @@ class Workload:
     backward: bool
     dtype: str          # "f32" (fp32 in/out, rounded to bf16 on load) or "bf16"
     seed: int
+    Hkv: int = 0        # K/V heads shared by groups of query heads; 0: H (multi-head)
 
     @property
     def shape(self):
         return (self.B, self.H, self.N, self.d)
+
+    @property
+    def kv_heads(self):
+        return self.Hkv or self.H
 
     @property
     def scale(self):
@@ -49,24 +55,32 @@ WORKLOADS = [
     Workload("fwdbwd_causal_b4h16n4096d128", 4, 16, 4096, 128, True, True, "bf16", 5),
 ]
 
+# Grouped-query attention: 32 query heads sharing 8 K/V heads (groups of 4).
+GQA_WORKLOADS = [
+    Workload("fwdbwd_causal_gqa_b4h32kv8n4096d128", 4, 32, 4096, 128, True, True, "bf16", 6, 8),
+]
+
 
 def by_name(name: str) -> Workload:
-    for w in WORKLOADS:
+    for w in WORKLOADS + GQA_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)
 
 
-def draw(shape, seed, with_grad=False, dtype="bf16"):
+def draw(shape, seed, with_grad=False, dtype="bf16", kv_heads=None):
     """Return CPU tensors (q, k, v[, do]) drawn i.i.d. N(0,1) from ``seed``.
 
     dtype "bf16": rounded to torch.bfloat16; "f32": left in float32.
+    kv_heads: heads of k and v (default: those of ``shape``).
     """
     g = torch.Generator(device="cpu").manual_seed(int(seed))
     names = ["q", "k", "v"] + (["do"] if with_grad else [])
+    kv_shape = tuple(shape) if kv_heads is None else (shape[0], kv_heads, shape[2], shape[3])
     out = []
-    for _ in names:
-        x = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    for name in names:
+        x = torch.randn(kv_shape if name in ("k", "v") else tuple(shape), generator=g,
+                        dtype=torch.float32)
         if dtype == "bf16":
             x = x.to(torch.bfloat16)
         elif dtype != "f32":
@@ -76,7 +90,7 @@ def draw(shape, seed, with_grad=False, dtype="bf16"):
 
 
 def draw_workload(w: Workload):
-    return draw(w.shape, w.seed, with_grad=w.backward, dtype=w.dtype)
+    return draw(w.shape, w.seed, with_grad=w.backward, dtype=w.dtype, kv_heads=w.kv_heads)
 
 
 def to_f64(x: torch.Tensor):

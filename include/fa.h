@@ -48,7 +48,7 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,      /* a required pointer is NULL */
-    FA_ERR_SHAPE = 2,     /* B, H or N negative, or the grid would overflow */
+    FA_ERR_SHAPE = 2,     /* B, H or N negative, K/V heads not dividing H, or too large */
     FA_ERR_HEADDIM = 3,   /* d not in {64, 128} */
     FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
     FA_ERR_ARG = 5,       /* causal not 0/1, or scale not finite */
@@ -133,6 +133,42 @@ int fa_backward_grads(const void* q, const void* k, const void* v, const void* d
                       const float* lse, void* dq, void* dk, void* dv,
                       int B, int H, int N, int d, float scale, int causal,
                       const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Grouped-query and multi-query attention (nearauto.com FlashAttention-2
+ * article, section "新機能": each set of query heads shares a single key
+ * and value head, between multi-head and multi-query attention). H query
+ * heads share H_kv key/value heads: query head h reads K/V head
+ * h / (H / H_kv), i.e. consecutive groups of H / H_kv query heads share one
+ * K/V head (the page does not say which heads form a set; this is the plain
+ * reading). H_kv = H is multi-head attention, H_kv = 1 multi-query
+ * attention. H_kv < 1, or H_kv not dividing H, returns FA_ERR_SHAPE (when
+ * H > 0); everything else as for the calls without _gqa.
+ *
+ * fa_forward_gqa: q, o [B,H,N,d]; k, v [B,H_kv,N,d]; lse [B,H,N].
+ */
+int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int N, int d, float scale, int causal,
+                   hipStream_t stream);
+
+/*
+ * fa_backward_gqa: q, o, dout, dq [B,H,N,d]; k, v, dk, dv [B,H_kv,N,d];
+ * lse [B,H,N]; workspace of fa_backward_workspace_size(B,H,N,d) bytes (the
+ * row terms are per query row). dk and dv of a K/V head are the sums of the
+ * gradients of its query heads (the chain rule for a shared input), formed
+ * inside one workgroup per K/V head and key block, with no atomics: results
+ * stay bitwise reproducible. fa_backward_prep (per query head, unchanged)
+ * followed by fa_backward_grads_gqa is equivalent.
+ */
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    int B, int H, int H_kv, int N, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int fa_backward_grads_gqa(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv,
+                          int B, int H, int H_kv, int N, int d, float scale, int causal,
+                          const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);

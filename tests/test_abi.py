@@ -38,7 +38,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_prep",
-            "fa_backward_grads", "fa_backward_workspace_size", "fa_strerror"} <= set(names)
+            "fa_backward_grads", "fa_backward_workspace_size", "fa_strerror",
+            "fa_forward_gqa", "fa_backward_gqa", "fa_backward_grads_gqa"} <= set(names)
     raw = ctypes.CDLL(fa.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), f"{name} declared in include/ but not exported"
@@ -152,8 +153,42 @@ def test_backward_stage_validation(lib):
     assert grads(ptrs=[NULL] * 8, N=0, w=NULL, wb=0) == FA_OK
 
 
+def test_grouped_validation(lib):
+    """H_kv must be at least 1 and divide H; the rest is checked as without _gqa."""
+    ws = 2 * 6 * 16 * 4
+
+    def fwd_g(H=6, Hkv=2, ptrs=None, N=16, d=64):
+        ptrs = ptrs or [P] * 5
+        return lib.fa_forward_gqa(*ptrs, 1, H, Hkv, N, d, 0.125, 1, NULL)
+
+    def bwd_g(H=6, Hkv=2, ptrs=None, N=16, d=64, wb=ws):
+        ptrs = ptrs or [P] * 9
+        return lib.fa_backward_gqa(*ptrs, 1, H, Hkv, N, d, 0.125, 1, P, wb, NULL)
+
+    def grads_g(H=6, Hkv=2, ptrs=None, N=16, d=64, wb=ws):
+        ptrs = ptrs or [P] * 8
+        return lib.fa_backward_grads_gqa(*ptrs, 1, H, Hkv, N, d, 0.125, 1, P, wb, NULL)
+
+    for call in (fwd_g, bwd_g, grads_g):
+        for H, Hkv in ((6, 4), (6, 0), (6, -1), (4, 8), (5, 2)):
+            assert call(H=H, Hkv=Hkv) == FA_ERR_SHAPE, (call.__name__, H, Hkv)
+        assert call(d=96) == FA_ERR_HEADDIM
+        assert call(H=-6) == FA_ERR_SHAPE
+        assert call(N=0, ptrs=[NULL] * {fwd_g: 5, bwd_g: 9, grads_g: 8}[call]) == FA_OK
+        assert call(H=0, Hkv=0, ptrs=[NULL] * {fwd_g: 5, bwd_g: 9, grads_g: 8}[call]) == FA_OK
+    for i in range(5):
+        ptrs = [P] * 5
+        ptrs[i] = NULL
+        assert fwd_g(ptrs=ptrs) == FA_ERR_NULL
+    assert bwd_g(wb=ws - 1) == FA_ERR_WORKSPACE
+    assert grads_g(wb=ws - 1) == FA_ERR_WORKSPACE
+
+
 def test_python_binding_without_gpu_raises_cleanly(lib):
     torch = pytest.importorskip("torch")
     q = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_forward(q, q, q)  # CPU tensors are refused before the library is called
+    k = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_forward_gqa(torch.zeros((1, 2, 4, 64), dtype=torch.bfloat16), k, k)

@@ -1,0 +1,158 @@
+"""GPU parity of grouped-query and multi-query attention (H query heads sharing
+H_kv K/V heads) through the C ABI, against the fp64 oracle."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_14_amd import (fa_backward, fa_backward_gqa, fa_backward_grads_gqa,
+                                   fa_backward_prep, fa_forward, fa_forward_gqa)
+from exact_io_aware_14_amd.inputs import GQA_WORKLOADS, draw, to_f64
+from parity import check_grad, check_lse, check_o, log, sample_heads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (B, H, H_kv, N, d, causal): groups of 2, 3 and 4, multi-query (H_kv = 1),
+# ragged lengths, both head dimensions
+CASES = [
+    (1, 4, 2, 200, 64, True), (2, 6, 3, 333, 128, False), (1, 4, 1, 257, 128, True),
+    (1, 8, 2, 1000, 128, True), (2, 4, 4, 130, 64, False), (1, 16, 8, 384, 64, True),
+    (1, 3, 1, 65, 128, False),
+]
+
+
+def _ids(cases):
+    return [f"B{b}H{h}kv{hk}N{n}d{d}{'c' if c else 'n'}" for b, h, hk, n, d, c in cases]
+
+
+def _inputs(case, seed, with_grad=False):
+    B, H, Hkv, N, d, causal = case
+    return draw((B, H, N, d), seed, with_grad=with_grad, kv_heads=Hkv)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids(CASES))
+def test_gqa_forward(case):
+    B, H, Hkv, N, d, causal = case
+    q, k, v = _inputs(case, 300 + N)
+    scale = 1.0 / math.sqrt(d)
+    log(f"case gqa forward {case}")
+    o, lse = fa_forward_gqa(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            g = oracle.kv_head(h, H, Hkv)
+            ro, rl = oracle.forward_head(to_f64(q[b, h]), to_f64(k[b, g]), to_f64(v[b, g]),
+                                         scale, causal)
+            check_o(o[b, h], ro, f"{case} b={b} h={h}")
+            check_lse(lse[b, h], rl, f"{case} b={b} h={h}")
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids(CASES))
+def test_gqa_backward(case):
+    B, H, Hkv, N, d, causal = case
+    q, k, v, do = _inputs(case, 400 + N, with_grad=True)
+    scale = 1.0 / math.sqrt(d)
+    log(f"case gqa backward {case}")
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa_forward_gqa(qd, kd, vd, scale=scale, causal=causal)
+    dq, dk, dv = fa_backward_gqa(qd, kd, vd, o, dod, lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    assert tuple(dk.shape) == (B, Hkv, N, d) and tuple(dq.shape) == (B, H, N, d)
+    rq, rk, rv = oracle.backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal)
+    dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            check_grad(dq[b, h], rq[b, h], f"{case} b={b} h={h} dQ")
+        for g in range(Hkv):
+            check_grad(dk[b, g], rk[b, g], f"{case} b={b} kv={g} dK")
+            check_grad(dv[b, g], rv[b, g], f"{case} b={b} kv={g} dV")
+
+
+def test_gqa_with_all_heads_is_multi_head():
+    """H_kv = H runs the multi-head path: bitwise the result of the plain calls."""
+    shape = (2, 3, 257, 128)
+    q, k, v, do = (x.to(DEV) for x in draw(shape, 51, with_grad=True))
+    for causal in (False, True):
+        o1, l1 = fa_forward(q, k, v, causal=causal)
+        o2, l2 = fa_forward_gqa(q, k, v, causal=causal)
+        g1 = fa_backward(q, k, v, o1, do, l1, causal=causal)
+        g2 = fa_backward_gqa(q, k, v, o1, do, l1, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
+
+
+def test_gqa_matches_multi_head_on_repeated_kv():
+    """Grouped heads read the same K/V as multi-head attention on K/V copied to
+    every query head of the group: O, lse and dQ bitwise, and dK/dV equal to
+    the group sums of the multi-head gradients (up to their bf16 rounding)."""
+    B, H, Hkv, N, d = 1, 8, 2, 333, 128
+    q, k, v, do = (x.to(DEV) for x in draw((B, H, N, d), 52, with_grad=True, kv_heads=Hkv))
+    ke, ve = (x.repeat_interleave(H // Hkv, dim=1).contiguous() for x in (k, v))
+    for causal in (False, True):
+        o1, l1 = fa_forward_gqa(q, k, v, causal=causal)
+        o2, l2 = fa_forward(q, ke, ve, causal=causal)
+        dq1, dk1, dv1 = fa_backward_gqa(q, k, v, o1, do, l1, causal=causal)
+        dq2, dk2, dv2 = fa_backward(q, ke, ve, o2, do, l2, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(dq1, dq2)
+        for got, per_head in ((dk1, dk2), (dv1, dv2)):
+            summed = per_head.float().reshape(B, Hkv, H // Hkv, N, d).sum(2)
+            rel = ((got.float() - summed).norm() / summed.norm()).item()
+            assert rel < 4e-3, rel
+
+
+def test_gqa_stages_match_backward():
+    """fa_backward_prep + fa_backward_grads_gqa give bitwise fa_backward_gqa."""
+    B, H, Hkv, N, d = 2, 6, 2, 200, 64
+    q, k, v, do = (x.to(DEV) for x in draw((B, H, N, d), 53, with_grad=True, kv_heads=Hkv))
+    o, lse = fa_forward_gqa(q, k, v, causal=True)
+    ref = fa_backward_gqa(q, k, v, o, do, lse, causal=True)
+    ws = fa_backward_prep(o, do, lse)
+    got = fa_backward_grads_gqa(q, k, v, do, lse, ws, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
+def test_gqa_full_size_workload():
+    """The grouped workload at full size: sampled heads of O and a whole K/V
+    head's dK/dV (the sum over its 4 query heads) against the oracle."""
+    w = GQA_WORKLOADS[0]
+    log(f"workload {w.name}")
+    q, k, v, do = draw(w.shape, w.seed, with_grad=True, kv_heads=w.kv_heads)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa_forward_gqa(qd, kd, vd, scale=w.scale, causal=w.causal)
+    dq, dk, dv = fa_backward_gqa(qd, kd, vd, o, dod, lse, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    for x in (o, dq, dk, dv):
+        assert torch.isfinite(x.float()).all()
+    o = o.float().cpu().numpy()
+    for b, h in sample_heads(w.B, w.H, 2, seed=w.seed):
+        g = oracle.kv_head(h, w.H, w.kv_heads)
+        ro, _ = oracle.forward_head(to_f64(q[b, h]), to_f64(k[b, g]), to_f64(v[b, g]),
+                                    w.scale, w.causal)
+        check_o(o[b, h], ro, f"{w.name} b={b} h={h}")
+    b, g = 1, 5
+    group = w.H // w.kv_heads
+    rk = np.zeros((w.N, w.d))
+    rv = np.zeros((w.N, w.d))
+    dq = dq.float().cpu().numpy()
+    for h in range(g * group, (g + 1) * group):
+        rq, rk_h, rv_h = oracle.backward_head(to_f64(q[b, h]), to_f64(k[b, g]), to_f64(v[b, g]),
+                                              to_f64(do[b, h]), w.scale, w.causal)
+        rk += rk_h
+        rv += rv_h
+        if h == g * group:
+            check_grad(dq[b, h], rq, f"{w.name} b={b} h={h} dQ")
+    check_grad(dk[b, g].float().cpu().numpy(), rk, f"{w.name} b={b} kv={g} dK")
+    check_grad(dv[b, g].float().cpu().numpy(), rv, f"{w.name} b={b} kv={g} dV")
