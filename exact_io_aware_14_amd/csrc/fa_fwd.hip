@@ -117,13 +117,18 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
   int bh, qbr;
   const int L = blockIdx.x;
   if (p.xcd_remap) {
-    // consecutive workgroups go to the 8 XCDs in turn; give each XCD whole
+    // Consecutive workgroups go to the 8 XCDs in turn; each XCD gets whole
     // K/V heads (with all query heads that read them) so the K/V of a head
     // is re-read from that XCD's L2. Query head bh reads K/V head
     // bh / group: the query heads of K/V head kv are kv*group .. +group-1.
-    const int xcd = L & 7, idx = L >> 3, slot = idx / p.nqb;
+    // Within an XCD the blocks go out rank by rank under the causal mask
+    // (every head's longest block, then every head's next one), which
+    // balances the uneven block lengths; head by head otherwise, which keeps
+    // fewer heads' K/V in flight.
+    const int xcd = L & 7, idx = L >> 3, hx = p.BH >> 3;
+    const int slot = CAUSAL ? idx % hx : idx / p.nqb;
     bh = ((slot / p.group) * 8 + xcd) * p.group + slot % p.group;
-    qbr = idx % p.nqb;
+    qbr = CAUSAL ? idx / hx : idx % p.nqb;
   } else {
     bh = L % p.BH;
     qbr = L / p.BH;
