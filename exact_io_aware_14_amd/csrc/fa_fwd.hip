@@ -1,5 +1,6 @@
 // Forward exact attention for gfx950: one workgroup per (batch, head, block
-// of 256 query rows), eight waves of 32 query rows each.
+// of 128 query rows), four waves of 32 query rows each, two workgroups per
+// CU.
 //
 // Method: the tiled forward with a running row maximum m and row sum l, in
 // which the partial output of earlier key tiles is rescaled whenever m grows
@@ -24,20 +25,13 @@
 // tile through the transposing LDS read.
 //
 // K and V tiles move from global memory into LDS with buffer loads that
-// write LDS directly (no registers, no VALU), double-buffered and issued two
-// phases ahead of their first use. fp32 inputs take the same path through
-// registers, rounded to bf16.
-//
-// Schedule ("ping-pong"): the eight waves form two groups of four, one wave
-// of each group per SIMD. Work alternates between an MFMA phase X(t) =
-// {O += V_{t-1}^T P_{t-1}, S_t = K_t Q^T} and a VALU phase V(t) = {masks,
-// online softmax of S_t, P_t}, and the second group runs one phase behind
-// the first, with a workgroup barrier between phases: while one wave of a
-// SIMD issues its MFMAs (at raised priority) the other computes its
-// softmax, so the matrix cores and the vector ALUs work at the same time
-// (the interleaving principle the deepfa.ir page describes for
-// FlashAttention-3, here across waves of one SIMD rather than asynchronous
-// tensor-core instructions).
+// write LDS directly (no registers, no VALU), double-buffered: tile t+1
+// loads while tile t is computed, with one workgroup barrier per tile. The
+// two stages of K and of V are four separate LDS arrays and the tile loop
+// is unrolled by two, so every LDS read names the array it reads: the
+// compiler then sees that the loads in flight (into the other stage) cannot
+// alias it, and does not make the transposing reads wait for them. fp32
+// inputs take the same path through registers, rounded to bf16.
 #include <type_traits>
 
 #include "fa_common.h"
@@ -68,40 +62,27 @@ struct FwdParams {
   int xcd_remap; // K/V heads grouped per XCD (requires BH / group % 8 == 0)
 };
 
-template <int D, int BC, int WAVES>
+// Workgroup shape: four waves (128 query rows), two workgroups per CU; the
+// two waves a SIMD holds belong to different workgroups and overlap freely.
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
+
+template <int D, int BC>
 struct Layout {
-  static constexpr int kTileBytes = BC * D * 2;
-  static constexpr int kK = 0;                // K stages 0, 1 (row-major, rsw)
-  static constexpr int kV = 2 * kTileBytes;   // V stages 0, 1 (row-major, rsw)
-  static constexpr int kBytes = 4 * kTileBytes;
-  static constexpr int kFill = kTileBytes / 1024 / WAVES;  // 1 KB blocks per wave and tile
-  static_assert(kFill >= 1 && kTileBytes % (1024 * WAVES) == 0, "tile must split over waves");
+  static constexpr int kTileBytes = BC * D * 2;               // one stage of K or V (rsw)
+  static constexpr int kFill = kTileBytes / 1024 / kWaves;  // 1 KB blocks per wave and tile
+  static_assert(kFill >= 1 && kTileBytes % (1024 * kWaves) == 0, "tile must split over waves");
 };
 
-// Workgroup shapes. kSequential: 4 waves (128 query rows), two workgroups per
-// CU, each wave running its tiles as MFMA -> VALU -> MFMA; the two waves a
-// SIMD holds belong to different workgroups and overlap freely.
-// kPingPong: 8 waves (256 rows) in two groups of four, one wave of each
-// group per SIMD (waves w and w+4 share a SIMD), the groups one phase apart
-// at workgroup barriers so that one wave's MFMA phase meets the other's VALU
-// phase.
-enum Schedule { kSequential = 4, kPingPong = 8 };
-
-template <int WAVES>
-struct Shape {
-  static constexpr int kThreads = WAVES * 64;
-  static constexpr int kBR = WAVES * kRowsPerWave;  // query rows per workgroup
-  static constexpr int kMinBlocks = WAVES == kPingPong ? 1 : 2;
-};
-
-template <int D, int BC, int WAVES, bool CAUSAL, typename TIn, typename TOut>
-__global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) void fwd_kernel(
-    FwdParams p) {
-  using LY = Layout<D, BC, WAVES>;
-  constexpr int kBR = Shape<WAVES>::kBR;
-  constexpr int kThreads = Shape<WAVES>::kThreads;
-  constexpr int kRowsPerGroup = 4 * kRowsPerWave;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[LY::kBytes];
+template <int D, int BC, bool CAUSAL, typename TIn, typename TOut>
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
+  using LY = Layout<D, BC>;
+  // stages 0 and 1 of the K and V tiles (row-major, swizzle rsw)
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[LY::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[LY::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[LY::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[LY::kTileBytes];
   constexpr int kDK = D / 16;   // MFMA steps along d for S^T
   constexpr int kDB = D / 32;   // 32-row blocks of O^T
   constexpr int kKB = BC / 32;  // 32-key blocks of a tile
@@ -109,7 +90,6 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;  // ping-pong: 0 leads, 1 follows one phase behind
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -143,7 +123,7 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
   const TIn* vg = reinterpret_cast<const TIn*>(p.v) + kv_off;
 
   const int q0 = qb * kBR;                                        // first row of the block
-  const int qw0 = q0 + grp * kRowsPerGroup + (wave & 3) * kRowsPerWave;  // this wave's
+  const int qw0 = q0 + wave * kRowsPerWave;                       // this wave's
   const int myq = qw0 + col;                                      // this lane's row
   const int wave_last = min(qw0 + kRowsPerWave, N) - 1;
 
@@ -171,8 +151,8 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
   uint32_t fk[LY::kFill], fv[LY::kFill];  // direct-fill offsets of this lane
 #pragma unroll
   for (int i = 0; i < LY::kFill; ++i) {
-    fk[i] = fill_lane_offset<D, BC, WAVES>(i, wave, lane);
-    fv[i] = fill_lane_offset<D, BC, WAVES>(i, wave, lane);
+    fk[i] = fill_lane_offset<D, BC, kWaves>(i, wave, lane);
+    fv[i] = fill_lane_offset<D, BC, kWaves>(i, wave, lane);
   }
 
   f32x16 oacc[kDB];
@@ -189,12 +169,12 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
   const int wtiles = qw0 >= N ? 0 : (CAUSAL ? wave_last / BC + 1 : ktiles_all);
   const float c = p.c;
 
-  auto fill_tile = [&](const TIn* g, int t, int base, const uint32_t* lane_off) {
+  // start loading key tile t of g (K or V) into the stage array dst
+  auto fill_tile = [&](const TIn* g, int t, unsigned char* dst, const uint32_t* lane_off) {
     const int key0 = t * BC;
     const auto r = make_rsrc(g + (size_t)key0 * D, (uint32_t)(N - key0) * D * sizeof(TIn));
-    unsigned char* dst = smem + base + (t & 1) * LY::kTileBytes;
     if constexpr (sizeof(TIn) == 2) {
-      fill_direct<D, BC, WAVES>(dst, r, lane_off, wave);
+      fill_direct<D, BC, kWaves>(dst, r, lane_off, wave);
     } else {
       fill_f32<D, BC, kThreads>(reinterpret_cast<uint16_t*>(dst), r, 0, tid);
     }
@@ -203,8 +183,7 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
   // MFMA phase, first half: O^T += V^T P^T for tile t (slots (kb, m) of P^T
   // are accumulator rows 8m..8m+7). All operand reads are issued before the
   // first product, so the LDS latency is paid once per half phase.
-  auto pv = [&](int t) {
-    const unsigned char* vs = smem + LY::kV + (t & 1) * LY::kTileBytes;
+  auto pv = [&](const unsigned char* vs) {
     bf16x8 a[kKB][2][kDB];
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -223,15 +202,12 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
 #pragma unroll
         for (int db = 0; db < kDB; ++db) oacc[db] = mfma32(a[kb][m][db], b, oacc[db]);
       }
-#ifndef FA_EXP_NOSGB
     __builtin_amdgcn_sched_group_barrier(0x100, 4 * kKB * kDB, 0);  // the LDS reads
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * kKB * kDB, 0);  // then the MFMAs
-#endif
   };
 
-  // MFMA phase, second half: S^T = K Q^T for tile t
-  auto qk = [&](int t) {
-    const unsigned char* ks = smem + LY::kK + (t & 1) * LY::kTileBytes;
+  // MFMA phase, second half: S^T = K Q^T for the K tile ks
+  auto qk = [&](const unsigned char* ks) {
     bf16x8 a[kDK][kKB];
 #pragma unroll
     for (int kk = 0; kk < kDK; ++kk)
@@ -243,10 +219,8 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
     for (int kk = 0; kk < kDK; ++kk)
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) s[kb] = mfma32(a[kk][kb], qreg[kk], s[kb]);
-#ifndef FA_EXP_NOSGB
     __builtin_amdgcn_sched_group_barrier(0x100, kDK * kKB, 0);  // the LDS reads
     __builtin_amdgcn_sched_group_barrier(0x008, kDK * kKB, 0);  // then the MFMAs
-#endif
   };
 
   // VALU phase: masks, online softmax and P for tile t
@@ -306,68 +280,29 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
     l_run += ls0 + ls1;
   };
 
-  // ---- phases. K_t is loaded in phase 2t-2 and read in phases 2t (leading
-  // group) and 2t+1 (following group); V_t is loaded in phase 2t and read in
-  // phases 2t+2 and 2t+3. Each stage is reloaded only after the barrier that
-  // ends its last read, and every wave waits for its own loads at the end of
-  // the phase before the one that first reads them.
-  auto mfma_phase = [&](int t) {
-    __builtin_amdgcn_s_setprio(1);
-    if (t >= 1 && t - 1 < wtiles) pv(t - 1);
-    // keep P (consumed above) and S (produced below) from being live at once
-    __builtin_amdgcn_sched_barrier(0);
-    if (t < wtiles) qk(t);
-    __builtin_amdgcn_s_setprio(0);
-  };
-  auto fills = [&](int t) {  // at the start of phase 2t
-    if (t + 1 < ntiles) fill_tile(kg, t + 1, LY::kK, fk);
-    if (t < ntiles) fill_tile(vg, t, LY::kV, fv);
-  };
-
-  fill_tile(kg, 0, LY::kK, fk);
-  if constexpr (WAVES == kSequential) {
-    // K and V of tile t+1 load while tile t is computed: one barrier per
-    // tile, after which tile t is in LDS for every wave and every wave is
-    // done with tile t-1, whose stages the loads of tile t+1 overwrite
-    fill_tile(vg, 0, LY::kV, fv);
-    for (int t = 0; t < ntiles; ++t) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (t + 1 < ntiles) {
-        fill_tile(kg, t + 1, LY::kK, fk);
-        fill_tile(vg, t + 1, LY::kV, fv);
-      }
-      if (t < wtiles) {
-        qk(t);
-        softmax(t);
-        pv(t);
-      }
-    }
-  } else {
+  // ---- tiles. K and V of tile t+1 load while tile t is computed: one
+  // barrier per tile, after which tile t is in LDS for every wave and every
+  // wave is done with tile t-1, whose stage the loads of tile t+1 overwrite.
+  // Even tiles use stage 0 (k0, v0), odd tiles stage 1 (k1, v1).
+  auto step = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
+                  unsigned char* vn) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // Each group has its own copy of the loop, so that only its own
-    // phase-crossing values (P for the leading group, S for the following
-    // one) stay live across iterations. Both copies pass the same barriers.
-    if (grp == 0) {
-      for (int t = 0; t <= ntiles; ++t) {
-        fills(t);
-        mfma_phase(t);                         // phase 2t:   X(t)
-        __syncthreads();
-        if (t < wtiles) softmax(t);            // phase 2t+1: V(t)
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
-    } else {
-      for (int t = 0; t <= ntiles; ++t) {
-        fills(t);
-        if (t >= 1 && t - 1 < wtiles) softmax(t - 1);  // phase 2t:   V(t-1)
-        __syncthreads();
-        mfma_phase(t);                                 // phase 2t+1: X(t)
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
+    if (t + 1 < ntiles) {
+      fill_tile(kg, t + 1, kn, fk);
+      fill_tile(vg, t + 1, vn, fv);
     }
+    if (t < wtiles) {
+      qk(kc);
+      softmax(t);
+      pv(vc);
+    }
+  };
+  fill_tile(kg, 0, k0, fk);
+  fill_tile(vg, 0, v0, fv);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, k0, v0, k1, v1);
+    if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
   }
 
   // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2
@@ -397,11 +332,6 @@ __global__ __launch_bounds__(Shape<WAVES>::kThreads, Shape<WAVES>::kMinBlocks) v
 }
 
 constexpr int kBC = 64;  // keys per tile
-#ifndef FA_EXP_SCHEDULE
-constexpr int kSchedule = kSequential;
-#else
-constexpr int kSchedule = FA_EXP_SCHEDULE;
-#endif
 
 template <int D, bool CAUSAL, typename TIn, typename TOut>
 hipError_t launch_typed(const FwdArgs& a) {
@@ -415,15 +345,15 @@ hipError_t launch_typed(const FwdArgs& a) {
   p.H = a.H;
   p.group = a.H / a.Hkv;
   p.N = a.N;
-  p.nqb = (a.N + Shape<kSchedule>::kBR - 1) / Shape<kSchedule>::kBR;
+  p.nqb = (a.N + kBR - 1) / kBR;
   // c is kept positive: a zero or denormal scale is raised to 1e-30, which
   // changes no score by more than 1e-27 and keeps c * (-inf) = -inf
   p.c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   p.negate_q = a.scale < 0.0f;
   p.xcd_remap = (p.BH / p.group) % 8 == 0;
   dim3 grid((unsigned)((long long)p.BH * p.nqb));
-  hipLaunchKernelGGL((fwd_kernel<D, kBC, kSchedule, CAUSAL, TIn, TOut>), grid,
-                     dim3(Shape<kSchedule>::kThreads), 0, a.stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, kBC, CAUSAL, TIn, TOut>), grid,
+                     dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
 }
 
@@ -441,7 +371,7 @@ hipError_t launch_forward_bf16(const FwdArgs& a) { return launch_dtype<uint16_t,
 hipError_t launch_forward_f32(const FwdArgs& a) { return launch_dtype<float, float>(a); }
 
 long long forward_grid_size(int B, int H, int N) {
-  return (long long)B * H * ((N + Shape<kSchedule>::kBR - 1) / Shape<kSchedule>::kBR);
+  return (long long)B * H * ((N + kBR - 1) / kBR);
 }
 
 }  // namespace fa
