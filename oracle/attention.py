@@ -20,6 +20,12 @@ What it computes (per batch b and head h, all heads independent):
 * Causal masking (keys j <= query i visible) is named but never defined on the
   pages; the plainest reading, the lower-triangular mask with equal query and
   key lengths, is used.
+* Local (sliding-window) attention is named on the pages only as a coming
+  variant (nearauto.com page, section "今後の仕事"; aiunderstanding.org page,
+  section "Il futuro dell'attenzione flash"). The reading used generalises
+  the causal mask: every function's ``causal`` argument may also be a pair
+  (left, right), key j visible to query i iff i - left <= j <= i + right, a
+  bound of -1 meaning none on that side; True is (-1, 0), False (-1, -1).
 * The per-row logsumexp lse_i = ln sum_j exp(scale * q_i . k_j) over visible
   keys is not on the pages; it is the row statistic the backward pass needs
   to recompute P without storing it (deepfa.ir page, section
@@ -61,12 +67,31 @@ def _check_head(q, k, v):
         raise ValueError("shape mismatch between q, k, v")
 
 
+def window_bounds(causal):
+    """(left, right) of a mask argument: key j is visible to query i iff
+    (left < 0 or j >= i - left) and (right < 0 or j <= i + right).
+
+    ``causal`` is False (every key), True (keys j <= i: (-1, 0)) or a pair
+    (left, right) of integers >= -1 (a local / sliding-window mask; -1: no
+    bound on that side)."""
+    if causal is None or isinstance(causal, (bool, np.bool_)):
+        return (-1, 0) if causal else (-1, -1)
+    left, right = (int(x) for x in causal)
+    if left < -1 or right < -1:
+        raise ValueError(f"window bounds must be >= -1, got {causal}")
+    return left, right
+
+
 def _scores(q_rows, k, scale, row_ids, causal):
     """S = scale * Q K^T for the given query rows, masked keys set to -inf."""
     s = scale * (q_rows @ k.T)
-    if causal:
-        keys = np.arange(k.shape[0])[None, :]
-        s = np.where(keys <= row_ids[:, None], s, -np.inf)
+    left, right = window_bounds(causal)
+    keys = np.arange(k.shape[0])[None, :]
+    rows = row_ids[:, None]
+    if left >= 0:
+        s = np.where(keys >= rows - left, s, -np.inf)
+    if right >= 0:
+        s = np.where(keys <= rows + right, s, -np.inf)
     return s
 
 

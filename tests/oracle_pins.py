@@ -354,7 +354,78 @@ def pin_gqa_finite_differences():
                    f"grouped finite differences input {which} H={heads} Hkv={kv_heads}")
 
 
+# ---------------------------------------------------------------- local (sliding-window) masks
+
+WINDOWS = ((0, 0), (3, 0), (2, 1), (-1, 2), (4, -1), (1, 5), (0, -1))
+
+
+def _torch_window_mask(n, left, right):
+    """Visible-key mask built from torch.tril / torch.triu (no index arithmetic)."""
+    ones = torch.ones(n, n, dtype=torch.bool)
+    mask = ones.clone()
+    if right >= 0:
+        mask &= ones.tril(right)
+    if left >= 0:
+        mask &= ones.triu(-left)
+    return mask
+
+
+def pin_window_special_cases():
+    rng = np.random.default_rng(31)
+    for n, d in ((7, 3), (12, 5)):
+        q, k, v = _rand_head(rng, n, d)
+        for scale in (0.6, -1.3):
+            # (-1, 0) is the causal mask, (-1, -1) none at all: exactly the same arithmetic
+            for win, flag in (((-1, 0), True), ((-1, -1), False)):
+                o1, l1 = A.forward_head(q, k, v, scale, win)
+                o2, l2 = A.forward_head(q, k, v, scale, flag)
+                assert np.array_equal(o1, o2) and np.array_equal(l1, l2), f"window {win}"
+            # (0, 0): every row sees only its own key
+            o, lse = A.forward_head(q, k, v, scale, (0, 0))
+            _close(o, v, 1e-14, "window (0,0) returns V")
+            _close(lse, scale * np.sum(q * k, axis=1), 1e-13, "window (0,0) lse")
+
+
+def pin_window_vs_torch():
+    rng = np.random.default_rng(32)
+    for n, d in ((9, 4), (16, 3)):
+        for left, right in WINDOWS:
+            q, k, v = _rand_head(rng, n, d)
+            do = rng.standard_normal((n, d))
+            scale = 0.7
+            mask = _torch_window_mask(n, left, right)
+            t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v)]
+            sc = (t[0] @ t[1].T * scale).masked_fill(~mask, -math.inf)
+            o_t = torch.softmax(sc, dim=-1) @ t[2]
+            (o_t * torch.tensor(do)).sum().backward()
+            o, lse = A.forward_head(q, k, v, scale, (left, right))
+            what = f"window ({left},{right}) n={n}"
+            _close(o, o_t.detach().numpy(), 1e-12, f"O vs torch {what}")
+            _close(lse, torch.logsumexp(sc, dim=-1).detach().numpy(), 1e-12, f"lse vs torch {what}")
+            grads = A.backward_head(q, k, v, do, scale, (left, right))
+            for name, mine, ref in zip(("dQ", "dK", "dV"), grads, t):
+                _close(mine, ref.grad.numpy(), 1e-11, f"{name} vs autograd {what}")
+
+
+def pin_window_brute_force():
+    rng = np.random.default_rng(33)
+    n, d, scale = 6, 2, 0.9
+    for left, right in WINDOWS:
+        q, k, v = _rand_head(rng, n, d)
+        o, lse = A.forward_head(q, k, v, scale, (left, right))
+        for i in range(n):
+            keys = [j for j in range(n)
+                    if (left < 0 or i - left <= j) and (right < 0 or j <= i + right)]
+            w = [math.exp(scale * sum(q[i, c] * k[j, c] for c in range(d))) for j in keys]
+            tot = sum(w)
+            for c in range(d):
+                ref = sum(wj * v[j, c] for wj, j in zip(w, keys)) / tot
+                assert abs(o[i, c] - ref) < 1e-12, f"brute force window ({left},{right}) row {i}"
+            assert abs(lse[i] - math.log(tot)) < 1e-12
+
+
 ALL_PINS = [pin_golden_forward, pin_golden_backward, pin_vs_torch_sdpa,
             pin_backward_vs_autograd, pin_finite_differences, pin_brute_force,
             pin_online_recurrence, pin_forward_invariants, pin_backward_invariants,
-            pin_gqa_vs_autograd, pin_gqa_finite_differences]
+            pin_gqa_vs_autograd, pin_gqa_finite_differences, pin_window_special_cases,
+            pin_window_vs_torch, pin_window_brute_force]

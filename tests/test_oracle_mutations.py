@@ -95,6 +95,24 @@ def _backward_not_summed(q, k, v, do, scale, causal):
     return dq, dk, dv
 
 
+def _window_variant(kind):
+    def scores(q_rows, k, scale, row_ids, causal):
+        s = scale * (q_rows @ k.T)
+        left, right = A.window_bounds(causal)
+        if kind == "swapped":
+            left, right = right, left
+        keys = np.arange(k.shape[0])[None, :]
+        rows = row_ids[:, None]
+        if left >= 0:
+            lo = rows - left + (1 if kind == "left_strict" else 0)
+            s = np.where(keys >= lo, s, -np.inf)
+        if right >= 0:
+            hi = rows + right + (1 if kind == "right_wide" else 0)
+            s = np.where(keys <= hi, s, -np.inf)
+        return s
+    return scores
+
+
 MUTATIONS = {
     "scale_dropped": ("_scores", _scores_no_scale),
     "causal_mask_flipped": ("_scores", _scores_flipped_mask),
@@ -111,6 +129,9 @@ MUTATIONS = {
     "gqa_head_map_modulo": ("kv_head", _kv_head_modulo),
     "gqa_head_map_reversed": ("kv_head", _kv_head_reversed),
     "gqa_grads_overwritten": ("backward", _backward_not_summed),
+    "window_left_bound_strict": ("_scores", _window_variant("left_strict")),
+    "window_bounds_swapped": ("_scores", _window_variant("swapped")),
+    "window_right_bound_one_wide": ("_scores", _window_variant("right_wide")),
 }
 
 
