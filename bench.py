@@ -18,10 +18,14 @@ timed on a bounded sample of the same workload on this host.
 A second object, `gqa`, times the same step on the grouped-query workload
 B=4, H=32 query heads sharing H_kv=8 K/V heads, N=4096, d=128, causal (seed
 6), through fa_forward_gqa, fa_backward_prep and fa_backward_grads_gqa; its
-FLOP count is that of 32 heads.
+FLOP count is that of 32 heads. A third, `window`, times it on the local
+workload B=4, H=16, N=4096, d=128 with a causal window of 1024 keys (seed
+7) through the _window calls; its FLOP count is 4*d per visible (query,
+key) pair, counted exactly.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-                       [--copy-calibration] [--no-gqa] [--gqa-only]
+                       [--copy-calibration] [--no-gqa] [--gqa-only] [--no-window]
+                       [--window-only]
 --copy-calibration first runs a plain device copy of 1 GiB (torch's copy
 kernel), whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic
 counters of the attention kernels in the same profiled run.
@@ -43,6 +47,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6
 WORKLOAD = "fwdbwd_causal_b4h16n4096d128"
 GQA_WORKLOAD = "fwdbwd_causal_gqa_b4h32kv8n4096d128"
+WINDOW_WORKLOAD = "fwdbwd_window1024_b4h16n4096d128"
 METRIC = "attention TFLOP/s (fwd, fwd+bwd) bf16 on 1 MI355X; % of MFMA peak"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["exact_io_aware_14_amd/csrc/fa_common.h", "exact_io_aware_14_amd/csrc/fa_fwd.hip",
@@ -57,8 +62,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def visible_pairs(n, left, right):
+    """(query, key) pairs of one head with i-left <= j <= i+right (-1: unbounded)."""
+    total = 0
+    for i in range(n):
+        lo = 0 if left < 0 else max(0, i - left)
+        hi = n - 1 if right < 0 else min(n - 1, i + right)
+        total += hi - lo + 1
+    return total
+
+
 def counted_flops(w):
-    fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    if w.window_left >= 0 or w.window_right >= 0:
+        fwd = 4.0 * w.B * w.H * w.d * visible_pairs(w.N, w.window_left, w.window_right)
+    else:
+        fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
     return fwd, 2.5 * fwd
 
 
@@ -120,44 +138,60 @@ def time_steps(step, steps, warmup, stream):
     return parts, sum(e[0].elapsed_time(e[3]) for e in events) / steps
 
 
-def measure_gqa(steps, warmup):
+def measure_variant(name, steps, warmup):
+    """The forward+backward step on a grouped-query or local-window workload,
+    through the calls that take those arguments."""
     import torch
 
-    from exact_io_aware_14_amd import (fa_backward_grads_gqa, fa_backward_prep,
-                                       fa_backward_workspace_size, fa_forward_gqa)
+    import exact_io_aware_14_amd as fa
     from exact_io_aware_14_amd.inputs import by_name, draw
 
-    w = by_name(GQA_WORKLOAD)
+    w = by_name(name)
     dev = torch.device("cuda:0")
     q, k, v, do = (x.to(dev) for x in draw(w.shape, w.seed, with_grad=True, kv_heads=w.kv_heads))
     o = torch.empty_like(q)
     lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa_backward_workspace_size(*w.shape), dtype=torch.uint8, device=dev)
+    ws = torch.empty(fa.fa_backward_workspace_size(*w.shape), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    window = w.window_left >= 0 or w.window_right >= 0
+    win = (w.window_left, w.window_right)
 
     def step(ev):
         if ev is not None:
             ev[0].record(stream)
-        fa_forward_gqa(q, k, v, w.scale, w.causal, o, lse, stream=stream)
+        if window:
+            fa.fa_forward_window(q, k, v, *win, w.scale, o, lse, stream=stream)
+        else:
+            fa.fa_forward_gqa(q, k, v, w.scale, w.causal, o, lse, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        fa_backward_prep(o, do, lse, ws, stream=stream)
+        fa.fa_backward_prep(o, do, lse, ws, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        fa_backward_grads_gqa(q, k, v, do, lse, ws, w.scale, w.causal, dq, dk, dv, stream=stream)
+        if window:
+            fa.fa_backward_grads_window(q, k, v, do, lse, ws, *win, w.scale, dq, dk, dv,
+                                        stream=stream)
+        else:
+            fa.fa_backward_grads_gqa(q, k, v, do, lse, ws, w.scale, w.causal, dq, dk, dv,
+                                     stream=stream)
         if ev is not None:
             ev[3].record(stream)
 
     (fwd_ms, prep_ms, grads_ms), step_ms = time_steps(step, steps, warmup, stream)
     fwd_f, bwd_f = counted_flops(w)
-    return {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d,
-            "causal": w.causal, "steps": steps,
-            "fwdbwd_tflops": round((fwd_f + bwd_f) / (step_ms * 1e-3) / 1e12, 2),
-            "fwd_tflops": round(fwd_f / (fwd_ms * 1e-3) / 1e12, 2),
-            "bwd_tflops": round(bwd_f / ((prep_ms + grads_ms) * 1e-3) / 1e12, 2),
-            "ms": {"fwd": round(fwd_ms, 4), "bwd_prep": round(prep_ms, 4),
-                   "bwd_grads": round(grads_ms, 4)}}
+    out = {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d}
+    if window:
+        out["window"] = [w.window_left, w.window_right]
+    else:
+        out["causal"] = w.causal
+    out.update({"steps": steps,
+                "fwdbwd_tflops": round((fwd_f + bwd_f) / (step_ms * 1e-3) / 1e12, 2),
+                "fwd_tflops": round(fwd_f / (fwd_ms * 1e-3) / 1e12, 2),
+                "bwd_tflops": round(bwd_f / ((prep_ms + grads_ms) * 1e-3) / 1e12, 2),
+                "ms": {"fwd": round(fwd_ms, 4), "bwd_prep": round(prep_ms, 4),
+                       "bwd_grads": round(grads_ms, 4)}})
+    return out
 
 
 def copy_calibration():
@@ -182,6 +216,9 @@ def main():
     ap.add_argument("--no-gqa", action="store_true")
     ap.add_argument("--gqa-only", action="store_true",
                     help="time only the grouped-query step (for its profile)")
+    ap.add_argument("--no-window", action="store_true")
+    ap.add_argument("--window-only", action="store_true",
+                    help="time only the local-window step (for its profile)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -191,7 +228,12 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     if args.gqa_only:
-        print(json.dumps({"gqa": measure_gqa(args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"gqa": measure_variant(GQA_WORKLOAD, args.steps, args.warmup)}),
+              flush=True)
+        return
+    if args.window_only:
+        print(json.dumps({"window": measure_variant(WINDOW_WORKLOAD, args.steps, args.warmup)}),
+              flush=True)
         return
 
     import torch
@@ -286,7 +328,9 @@ def main():
         "roofline": roofline,
     }
     if not args.no_gqa:
-        out["gqa"] = measure_gqa(args.steps, args.warmup)
+        out["gqa"] = measure_variant(GQA_WORKLOAD, args.steps, args.warmup)
+    if not args.no_window:
+        out["window"] = measure_variant(WINDOW_WORKLOAD, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
     print(json.dumps(out), flush=True)

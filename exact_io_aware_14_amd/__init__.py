@@ -13,8 +13,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["FAError", "fa_forward", "fa_forward_gqa", "fa_forward_f32", "fa_backward",
-           "fa_backward_gqa", "fa_backward_prep", "fa_backward_grads", "fa_backward_grads_gqa",
+__all__ = ["FAError", "fa_forward", "fa_forward_gqa", "fa_forward_window", "fa_forward_f32",
+           "fa_backward", "fa_backward_gqa", "fa_backward_window", "fa_backward_prep",
+           "fa_backward_grads", "fa_backward_grads_gqa", "fa_backward_grads_window",
            "fa_backward_workspace_size", "fa_strerror", "library", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -46,7 +47,12 @@ def library():
                 ("fa_backward_gqa", [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
                                      vp, sz, vp]),
                 ("fa_backward_grads_gqa", [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
-                                           vp, sz, vp])):
+                                           vp, sz, vp]),
+                ("fa_forward_window", [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]),
+                ("fa_backward_window", [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
+                                        i, vp, sz, vp]),
+                ("fa_backward_grads_window", [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f,
+                                              i, i, vp, sz, vp])):
             if hasattr(lib, name):  # an older build without them fails when they are called
                 getattr(lib, name).argtypes = argtypes
                 getattr(lib, name).restype = i
@@ -107,7 +113,7 @@ def _kv_heads(q, k):
     return k.shape[1]
 
 
-def _forward(fn_name, q, k, v, scale, causal, o, lse, stream, dtype, gqa=False):
+def _forward(fn_name, q, k, v, scale, causal, o, lse, stream, dtype, gqa=False, window=None):
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
@@ -126,9 +132,9 @@ def _forward(fn_name, q, k, v, scale, causal, o, lse, stream, dtype, gqa=False):
     if scale is None:
         scale = d ** -0.5
     heads = (B, H, Hkv) if gqa else (B, H)
+    mask = (int(window[0]), int(window[1])) if window is not None else (int(bool(causal)),)
     st = getattr(library(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                     *heads, N, d, float(scale), int(bool(causal)),
-                                     _stream(stream))
+                                     *heads, N, d, float(scale), *mask, _stream(stream))
     if st != 0:
         raise FAError(st, fn_name)
     return o, lse
@@ -145,6 +151,15 @@ def fa_forward_gqa(q, k, v, scale=None, causal=False, o=None, lse=None, stream=N
     dividing H (see fa_forward_gqa in fa.h)."""
     return _forward("fa_forward_gqa", q, k, v, scale, causal, o, lse, stream,
                     _torch().bfloat16, gqa=True)
+
+
+def fa_forward_window(q, k, v, window_left, window_right, scale=None, o=None, lse=None,
+                      stream=None):
+    """Local-window forward: key j visible to query i iff
+    i - window_left <= j <= i + window_right (-1: no bound on that side); k, v
+    may have fewer heads than q (see fa_forward_window in fa.h)."""
+    return _forward("fa_forward_window", q, k, v, scale, None, o, lse, stream,
+                    _torch().bfloat16, gqa=True, window=(window_left, window_right))
 
 
 def fa_forward_f32(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None):
@@ -271,4 +286,45 @@ def fa_backward_grads_gqa(q, k, v, dout, lse, workspace, scale=None, causal=Fals
                                          _stream(stream))
     if st != 0:
         raise FAError(st, "fa_backward_grads_gqa")
+    return dq, dk, dv
+
+
+def fa_backward_window(q, k, v, o, dout, lse, window_left, window_right, scale=None, dq=None,
+                       dk=None, dv=None, workspace=None, stream=None):
+    """Local-window backward (see fa_backward_window in fa.h)."""
+    Hkv = _kv_heads(q, k)
+    shape, dev, (dq, dk, dv) = _bwd_check(
+        q, (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)), lse,
+        (("dq", dq), ("dk", dk), ("dv", dv)), Hkv)
+    ws, ws_bytes = _workspace(shape, dev, workspace)
+    B, H, N, d = shape
+    scale = d ** -0.5 if scale is None else scale
+    st = library().fa_backward_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d,
+                                      float(scale), int(window_left), int(window_right),
+                                      _ptr(ws), ws_bytes, _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_backward_window")
+    return dq, dk, dv
+
+
+def fa_backward_grads_window(q, k, v, dout, lse, workspace, window_left, window_right,
+                             scale=None, dq=None, dk=None, dv=None, stream=None):
+    """Second backward stage for local windows (see fa.h)."""
+    Hkv = _kv_heads(q, k)
+    shape, dev, (dq, dk, dv) = _bwd_check(
+        q, (("q", q), ("k", k), ("v", v), ("dout", dout)), lse,
+        (("dq", dq), ("dk", dk), ("dv", dv)), Hkv)
+    if workspace is None or workspace.device != dev:
+        raise ValueError("workspace from fa_backward_prep is required, on the same device")
+    B, H, N, d = shape
+    scale = d ** -0.5 if scale is None else scale
+    st = library().fa_backward_grads_window(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                            _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d,
+                                            float(scale), int(window_left), int(window_right),
+                                            _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_backward_grads_window")
     return dq, dk, dv

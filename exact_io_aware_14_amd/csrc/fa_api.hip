@@ -16,8 +16,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Checks shared by the forward and backward entry points, in the order
 // documented in fa.h. Returns FA_OK and sets *empty when there is nothing to
 // compute.
-int check_common(int B, int H, int Hkv, int N, int d, float scale, int causal, bool* empty) {
-  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+int check_common(int B, int H, int Hkv, int N, int d, float scale, int wl, int wr, bool* empty) {
+  if (wl < -1 || wr < -1) return FA_ERR_ARG;
   if (!isfinite(scale)) return FA_ERR_ARG;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
@@ -45,52 +45,58 @@ bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d) {
 }
 
 int forward_common(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                   int H, int Hkv, int N, int d, float scale, int causal, hipStream_t stream,
+                   int H, int Hkv, int N, int d, float scale, int wl, int wr, hipStream_t stream,
                    bool f32) {
   bool empty = false;
-  int st = check_common(B, H, Hkv, N, d, scale, causal, &empty);
+  int st = check_common(B, H, Hkv, N, d, scale, wl, wr, &empty);
   if (st != FA_OK || empty) return st;
   const void* ptrs[5] = {q, k, v, o, lse};
   st = check_ptrs(ptrs, 5);
   if (st != FA_OK) return st;
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal, stream, Hkv};
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, wl, wr, stream, Hkv};
   hipError_t e = f32 ? fa::launch_forward_f32(a) : fa::launch_forward_bf16(a);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int grads_common(const void* q, const void* k, const void* v, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
-                 int d, float scale, int causal, const void* workspace, size_t workspace_bytes,
-                 hipStream_t stream) {
+                 int d, float scale, int wl, int wr, const void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
   bool empty = false;
-  int st = check_common(B, H, Hkv, N, d, scale, causal, &empty);
+  int st = check_common(B, H, Hkv, N, d, scale, wl, wr, &empty);
   if (st != FA_OK || empty) return st;
   const void* ptrs[8] = {q, k, v, dout, lse, dq, dk, dv};
   st = check_ptrs(ptrs, 8);
   if (st != FA_OK) return st;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
   fa::BwdArgs a{q, k, v, nullptr, dout, lse, dq, dk, dv,
-                static_cast<float*>(const_cast<void*>(workspace)), B, H, N, d, scale, causal,
+                static_cast<float*>(const_cast<void*>(workspace)), B, H, N, d, scale, wl, wr,
                 stream, Hkv};
   return fa::launch_backward_grads(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int backward_common(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
-                    int H, int Hkv, int N, int d, float scale, int causal, void* workspace,
+                    int H, int Hkv, int N, int d, float scale, int wl, int wr, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   bool empty = false;
-  int st = check_common(B, H, Hkv, N, d, scale, causal, &empty);
+  int st = check_common(B, H, Hkv, N, d, scale, wl, wr, &empty);
   if (st != FA_OK || empty) return st;
   const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
   st = check_ptrs(ptrs, 9);
   if (st != FA_OK) return st;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace),
-                B, H, N, d, scale, causal, stream, Hkv};
+                B, H, N, d, scale, wl, wr, stream, Hkv};
   if (fa::launch_backward_prep(a) != hipSuccess) return FA_ERR_HIP;
   return fa::launch_backward_grads(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+// The causal flag of the entry points without a window: 1 is the window
+// (-1, 0), 0 no mask; anything else is FA_ERR_ARG, reported as an invalid
+// bound.
+int causal_left(int causal) { return (causal == 0 || causal == 1) ? -1 : -2; }
+int causal_right(int causal) { return causal == 1 ? 0 : (causal == 0 ? -1 : -2); }
 
 }  // namespace
 
@@ -98,17 +104,20 @@ extern "C" {
 
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int N, int d, float scale, int causal, hipStream_t stream) {
-  return forward_common(q, k, v, o, lse, B, H, H, N, d, scale, causal, stream, false);
+  return forward_common(q, k, v, o, lse, B, H, H, N, d, scale, causal_left(causal),
+                        causal_right(causal), stream, false);
 }
 
 int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int H, int H_kv, int N, int d, float scale, int causal, hipStream_t stream) {
-  return forward_common(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, stream, false);
+  return forward_common(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal_left(causal),
+                        causal_right(causal), stream, false);
 }
 
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
                    int H, int N, int d, float scale, int causal, hipStream_t stream) {
-  return forward_common(q, k, v, o, lse, B, H, H, N, d, scale, causal, stream, true);
+  return forward_common(q, k, v, o, lse, B, H, H, N, d, scale, causal_left(causal),
+                        causal_right(causal), stream, true);
 }
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
@@ -119,14 +128,14 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d) {
 int fa_backward_prep(const void* o, const void* dout, const float* lse, int B, int H, int N,
                      int d, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   bool empty = false;
-  int st = check_common(B, H, H, N, d, 1.0f, 0, &empty);
+  int st = check_common(B, H, H, N, d, 1.0f, -1, -1, &empty);
   if (st != FA_OK || empty) return st;
   const void* ptrs[3] = {o, dout, lse};
   st = check_ptrs(ptrs, 3);
   if (st != FA_OK) return st;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
   fa::BwdArgs a{nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr, nullptr,
-                static_cast<float*>(workspace), B, H, N, d, 1.0f, 0, stream, H};
+                static_cast<float*>(workspace), B, H, N, d, 1.0f, -1, -1, stream, H};
   return fa::launch_backward_prep(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -134,32 +143,60 @@ int fa_backward_grads(const void* q, const void* k, const void* v, const void* d
                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int N,
                       int d, float scale, int causal, const void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
-  return grads_common(q, k, v, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal, workspace,
-                      workspace_bytes, stream);
+  return grads_common(q, k, v, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal_left(causal),
+                      causal_right(causal), workspace, workspace_bytes, stream);
 }
 
 int fa_backward_grads_gqa(const void* q, const void* k, const void* v, const void* dout,
                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv,
                           int N, int d, float scale, int causal, const void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
-  return grads_common(q, k, v, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal,
-                      workspace, workspace_bytes, stream);
+  return grads_common(q, k, v, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale,
+                      causal_left(causal), causal_right(causal), workspace, workspace_bytes,
+                      stream);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                 float scale, int causal, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
-  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal,
-                         workspace, workspace_bytes, stream);
+  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale,
+                         causal_left(causal), causal_right(causal), workspace, workspace_bytes,
+                         stream);
 }
 
 int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                     int H, int H_kv, int N, int d, float scale, int causal, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal,
-                         workspace, workspace_bytes, stream);
+  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale,
+                         causal_left(causal), causal_right(causal), workspace, workspace_bytes,
+                         stream);
+}
+
+int fa_forward_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int H_kv, int N, int d, float scale, int window_left,
+                      int window_right, hipStream_t stream) {
+  return forward_common(q, k, v, o, lse, B, H, H_kv, N, d, scale, window_left, window_right,
+                        stream, false);
+}
+
+int fa_backward_window(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                       int H, int H_kv, int N, int d, float scale, int window_left,
+                       int window_right, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale,
+                         window_left, window_right, workspace, workspace_bytes, stream);
+}
+
+int fa_backward_grads_window(const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv, int B, int H,
+                             int H_kv, int N, int d, float scale, int window_left,
+                             int window_right, const void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  return grads_common(q, k, v, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, window_left,
+                      window_right, workspace, workspace_bytes, stream);
 }
 
 const char* fa_strerror(int status) {
@@ -170,7 +207,8 @@ const char* fa_strerror(int status) {
       return "invalid shape: B, H or N negative, K/V heads not dividing H, or the problem too large";
     case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-    case FA_ERR_ARG: return "invalid argument: causal must be 0 or 1 and scale finite";
+    case FA_ERR_ARG:
+      return "invalid argument: causal must be 0 or 1, window bounds >= -1, scale finite";
     case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
     default: return "unknown status";

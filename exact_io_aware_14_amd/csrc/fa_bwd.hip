@@ -70,6 +70,7 @@ struct BwdParams {
   int nqb;          // dQ jobs (256-row blocks) per query head
   float c;          // scale * log2(e)
   float scale;
+  int wl, wr;       // masked kernels: key j visible to query i iff i-wl <= j <= i+wr
   int xcd_remap;
 };
 
@@ -284,8 +285,13 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
     dkacc[i] = zero16();
   }
 
-  const int ntiles = (N + kTile - 1) / kTile;
-  const int t0 = CAUSAL ? k0 / kTile : 0;  // earlier query rows see none of these keys
+  // Masked kernels (CAUSAL: a causal or local window): query row i sees key
+  // j iff j - wr <= i <= j + wl, so the block's keys k0 .. kend are seen by
+  // the rows of query tiles t0 .. ntiles-1 only.
+  const int kend = min(k0 + kKeyBlock, N) - 1;
+  const int t0 = CAUSAL ? max(0, k0 - p.wr) / kTile : 0;
+  const int ntiles = CAUSAL ? min(N - 1, kend + p.wl) / kTile + 1 : (N + kTile - 1) / kTile;
+  const int lo_row = mykey - p.wr, hi_row = mykey + p.wl;  // rows that see this lane's key
   const float c = p.c;
   const unsigned char* kb = smem + LY::kKb + kw * 32 * D * 2;  // this wave's key rows
   const unsigned char* vb = smem + LY::kVb + kw * 32 * D * 2;
@@ -341,7 +347,10 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g4 + i;
         float pr = fast_exp2(__builtin_fmaf(s[r], c, -l2v[i]));
-        if constexpr (MASK) pr = (r0 + rr + i < mykey) ? 0.0f : pr;
+        if constexpr (MASK) {
+          const int row = r0 + rr + i;
+          pr = (row < lo_row || row > hi_row) ? 0.0f : pr;
+        }
         pv[i] = pr;
         dsv[i] = pr * (dp[r] - drv[i]);
       }
@@ -387,23 +396,34 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
     else if (jq + 1 < p.group)
       fill(jq + 1, t0, (step + 1) & 1);
   };
-  // Causal: this wave's rows r0 .. r0+31 of tile t see all of its keys once
-  // r0 >= kw0 + 31; before that the tile crosses the diagonal (masked), and
-  // with r0 + 31 < kw0 it sees none. Each wave walks its masked tiles and
-  // its unmasked tiles in two loops (every iteration passes one barrier),
-  // so no loop holds both versions of the tile body.
-  // first tile that needs no mask (none needs one without the causal mask)
-  const int tm =
-      CAUSAL ? min(ntiles, max(t0, (kw0 + 31 - 32 * qh + kTile - 1) / kTile)) : t0;
+  // Masked kernels: this wave's rows r0 .. r0+31 of tile t and its keys
+  // kw0 .. kw0+31 all see each other for tiles tm1 .. tm2-1 (r0 >= kw0+31-wr
+  // and r0+31 <= kw0+wl); the tiles before and after cross a window edge
+  // (masked), or show the wave none of its keys (skipped). Each wave walks
+  // them in three loops (every iteration passes one barrier), so no loop
+  // holds both versions of the tile body. Causal: no tiles after tm2.
+  int tm1 = t0, tm2 = ntiles;
+  if (CAUSAL) {
+    tm1 = min(ntiles, max(t0, ceil_div(kw0 + 31 - p.wr - 32 * qh, kTile)));
+    tm2 = min(ntiles, max(tm1, floor_div(kw0 + p.wl - 32 * qh - 31, kTile) + 1));
+  }
+  auto visible = [&](int t) {
+    const int r0 = t * kTile + 32 * qh;
+    return r0 + 31 >= kw0 - p.wr && r0 <= kw0 + 31 + p.wl;
+  };
   if (t0 < ntiles) fill(0, t0, 0);
   for (int jq = 0; jq < p.group; ++jq) {
-    for (int t = t0; t < tm; ++t, ++step) {
+    for (int t = t0; t < tm1; ++t, ++step) {
       sync_fill(jq, t);
-      if (t * kTile + 32 * qh + 31 >= kw0) tile(t, step & 1, std::true_type());
+      if (visible(t)) tile(t, step & 1, std::true_type());
     }
-    for (int t = tm; t < ntiles; ++t, ++step) {
+    for (int t = tm1; t < tm2; ++t, ++step) {
       sync_fill(jq, t);
       tile(t, step & 1, std::false_type());
+    }
+    for (int t = tm2; t < ntiles; ++t, ++step) {
+      sync_fill(jq, t);
+      if (visible(t)) tile(t, step & 1, std::true_type());
     }
   }
 
@@ -481,10 +501,16 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
 #pragma unroll
   for (int i = 0; i < kDB; ++i) dqacc[i] = zero16();
 
+  // Masked kernels (CAUSAL: a causal or local window): row i sees keys
+  // i-wl .. i+wr. The workgroup walks key tiles kt0 .. ntiles-1, those that
+  // one of its rows sees; this wave computes on tiles wt0 .. wt1-1.
   const int ntiles_all = (N + kTile - 1) / kTile;
-  const int ntiles =
-      CAUSAL ? min(ntiles_all, (min(q0 + kQBlock, N) - 1) / kTile + 1) : ntiles_all;
-  const int wtiles = qw0 >= N ? 0 : (CAUSAL ? wave_last / kTile + 1 : ntiles_all);
+  const int qend = min(q0 + kQBlock, N) - 1;
+  const int kt0 = CAUSAL ? max(0, q0 - p.wl) / kTile : 0;
+  const int ntiles = CAUSAL ? min(N - 1, qend + p.wr) / kTile + 1 : ntiles_all;
+  const int wt0 = CAUSAL ? max(0, qw0 - p.wl) / kTile : 0;
+  const int wt1 = qw0 >= N ? wt0 : (CAUSAL ? min(N - 1, wave_last + p.wr) / kTile + 1 : ntiles_all);
+  const int lo_key = myq - p.wl, hi_key = myq + p.wr;  // keys this lane's row sees
   const float c = p.c;
 
   auto fill = [&](int t) {
@@ -493,7 +519,7 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
     fill_tile<D>(smem + LY::kVt + st * LY::kTileBytes, vg, r0, N, off, wave);
   };
 
-  // one key tile; MASK: it crosses the causal diagonal of this wave's rows
+  // one key tile; MASK: it crosses a window edge of this wave's rows
   auto tile = [&](int t, auto mask_c) {
     constexpr bool MASK = decltype(mask_c)::value;
     const int ST = t & 1;
@@ -525,7 +551,7 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
         float pr = fast_exp2(__builtin_fmaf(s[r], c, -l2));
         if constexpr (MASK) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          pr = key <= myq ? pr : 0.0f;
+          pr = (key < lo_key || key > hi_key) ? 0.0f : pr;
         }
         dsv[r] = pr * (dp[r] - dr);
       }
@@ -556,19 +582,30 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
     __syncthreads();
     if (t + 1 < ntiles) fill(t + 1);
   };
-  // Causal: key tile t is unmasked for all of this wave's rows while
-  // t*64 + 63 <= qw0, crosses the diagonal up to tile wtiles-1, and is
-  // invisible after. Unmasked and masked tiles run in two loops (every
+  // Key tile t shows all of its keys to all of this wave's rows for tiles
+  // tm1 .. tm2-1 (t*64 >= wave_last-wl and t*64+63 <= qw0+wr); the visible
+  // tiles before and after cross a window edge (masked). Three loops (every
   // iteration passes one barrier), so no loop holds both tile bodies.
-  const int tm = CAUSAL ? min(wtiles, max(0, (qw0 + 1) / kTile)) : wtiles;
-  fill(0);
-  for (int t = 0; t < tm; ++t) {
+  // Causal: no masked tiles before tm1 = kt0 = 0.
+  int tm1 = kt0, tm2 = wt1;
+  if (CAUSAL) {
+    tm1 = min(ntiles, max(kt0, ceil_div(wave_last - p.wl, kTile)));
+    tm2 = min(wt1, max(tm1, floor_div(qw0 + p.wr - (kTile - 1), kTile) + 1));
+  }
+  if (qw0 >= N) tm2 = tm1;  // no rows: every tile is skipped
+  auto visible = [&](int t) { return t >= wt0 && t < wt1; };
+  fill(kt0);
+  for (int t = kt0; t < tm1; ++t) {
+    sync_fill(t);
+    if (visible(t)) tile(t, std::true_type());
+  }
+  for (int t = tm1; t < tm2; ++t) {
     sync_fill(t);
     tile(t, std::false_type());
   }
-  for (int t = tm; t < ntiles; ++t) {
+  for (int t = tm2; t < ntiles; ++t) {
     sync_fill(t);
-    if (t < wtiles) tile(t, std::true_type());
+    if (visible(t)) tile(t, std::true_type());
   }
 
   if (myq < N) store_rows<D>(p.dq + (head + myq) * D, dqacc, p.scale, half);
@@ -603,6 +640,8 @@ BwdParams make_params(const BwdArgs& a) {
   p.nqb = (a.N + kQBlock - 1) / kQBlock;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
+  p.wl = a.wl < 0 ? kUnbounded : a.wl;
+  p.wr = a.wr < 0 ? kUnbounded : a.wr;
   p.xcd_remap = (p.BH / p.group) % 8 == 0;
   return p;
 }
@@ -634,8 +673,8 @@ hipError_t launch_backward_prep(const BwdArgs& a) {
 
 hipError_t launch_backward_grads(const BwdArgs& a) {
   if (a.d == 64)
-    return a.causal ? launch_grads_typed<64, true>(a) : launch_grads_typed<64, false>(a);
-  return a.causal ? launch_grads_typed<128, true>(a) : launch_grads_typed<128, false>(a);
+    return a.masked() ? launch_grads_typed<64, true>(a) : launch_grads_typed<64, false>(a);
+  return a.masked() ? launch_grads_typed<128, true>(a) : launch_grads_typed<128, false>(a);
 }
 
 long long backward_grid_size(int B, int H, int Hkv, int N) {

@@ -201,6 +201,10 @@ __device__ __forceinline__ void st_tr4(uint16_t* tile, int r0, int ch, const uin
 
 #define FA_LDS __attribute__((address_space(3)))
 
+// Integer division rounding toward -infinity / +infinity (b > 0).
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
+__device__ __forceinline__ int ceil_div(int a, int b) { return -floor_div(-a, b); }
+
 __device__ __forceinline__ bf16x4 tr_read(const uint16_t* p) {
   typedef __bf16 v4bf __attribute__((__vector_size__(4 * sizeof(__bf16))));
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(

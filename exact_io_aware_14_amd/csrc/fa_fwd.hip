@@ -60,10 +60,12 @@ struct FwdParams {
   float c;       // |scale| * log2(e), at least 1e-30
   int negate_q;  // scale < 0: Q is negated on load and |scale| is used
   int xcd_remap; // K/V heads grouped per XCD (requires BH / group % 8 == 0)
+  int wl, wr;    // masked kernels: key j visible to query i iff i-wl <= j <= i+wr
 };
 
-// Workgroup shape: four waves (128 query rows), two workgroups per CU; the
-// two waves a SIMD holds belong to different workgroups and overlap freely.
+// Workgroup shape: four waves (128 query rows), two workgroups per CU at
+// d = 128 (four at d = 64 with bf16 inputs, at most 128 VGPRs); the waves a SIMD holds belong
+// to different workgroups and overlap freely.
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
@@ -76,7 +78,7 @@ struct Layout {
 };
 
 template <int D, int BC, bool CAUSAL, typename TIn, typename TOut>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 && sizeof(TIn) == 2 ? 4 : 2) void fwd_kernel(FwdParams p) {
   using LY = Layout<D, BC>;
   // stages 0 and 1 of the K and V tiles (row-major, swizzle rsw)
   __shared__ __attribute__((aligned(1024))) unsigned char k0[LY::kTileBytes];
@@ -101,14 +103,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     // K/V heads (with all query heads that read them) so the K/V of a head
     // is re-read from that XCD's L2. Query head bh reads K/V head
     // bh / group: the query heads of K/V head kv are kv*group .. +group-1.
-    // Within an XCD the blocks go out rank by rank under the causal mask
-    // (every head's longest block, then every head's next one), which
-    // balances the uneven block lengths; head by head otherwise, which keeps
-    // fewer heads' K/V in flight.
+    // Within an XCD the heads go out in pairs under the causal mask, the
+    // blocks of a pair rank by rank (both heads' longest block, then the
+    // next), which balances the uneven block lengths while only about two
+    // heads' K/V are in flight; head by head without the mask, where all
+    // blocks are alike.
     const int xcd = L & 7, idx = L >> 3, hx = p.BH >> 3;
-    const int slot = CAUSAL ? idx % hx : idx / p.nqb;
+    const int g2 = (CAUSAL && hx % 2 == 0) ? 2 : 1;  // heads per group
+    const int grp = idx / (g2 * p.nqb), within = idx % (g2 * p.nqb);
+    const int slot = grp * g2 + within % g2;
     bh = ((slot / p.group) * 8 + xcd) * p.group + slot % p.group;
-    qbr = CAUSAL ? idx / hx : idx % p.nqb;
+    qbr = within / g2;
   } else {
     bh = L % p.BH;
     qbr = L / p.BH;
@@ -165,8 +170,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 
   const int ktiles_all = (N + BC - 1) / BC;
   // tiles the workgroup walks, and tiles with a visible key for this wave
-  const int ntiles = CAUSAL ? min(ktiles_all, (min(q0 + kBR, N) - 1) / BC + 1) : ktiles_all;
-  const int wtiles = qw0 >= N ? 0 : (CAUSAL ? wave_last / BC + 1 : ktiles_all);
+  // Masked kernels (CAUSAL: a causal or local window, bounds wl, wr; an
+  // unbounded side is 2^30): the workgroup walks key tiles t_first ..
+  // t_end-1, those holding a key that one of its rows sees, and each wave
+  // computes on the tiles [wt_first, wt_end) that hold one of its keys.
+  const int qlast = min(q0 + kBR, N) - 1;
+  const int t_first = CAUSAL ? max(0, q0 - p.wl) / BC : 0;
+  const int t_end = CAUSAL ? min(N - 1, qlast + p.wr) / BC + 1 : ktiles_all;
+  const int wt_first = CAUSAL ? max(0, qw0 - p.wl) / BC : 0;
+  const int wt_end = qw0 >= N ? wt_first : (CAUSAL ? min(N - 1, wave_last + p.wr) / BC + 1 : ktiles_all);
   const float c = p.c;
 
   // start loading key tile t of g (K or V) into the stage array dst
@@ -226,14 +238,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   // VALU phase: masks, online softmax and P for tile t
   auto softmax = [&](int t) {
     const int key0 = t * BC;
-    const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qw0);
+    // a tile needs masks where it passes N, the first row's upper bound or
+    // the last row's lower bound
+    const bool need_mask =
+        (key0 + BC > N) || (CAUSAL && (key0 + BC - 1 > qw0 + p.wr || key0 < wave_last - p.wl));
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          bool vis = key < N && (!CAUSAL || key <= myq);
+          bool vis = key < N && (!CAUSAL || (key <= myq + p.wr && key >= myq - p.wl));
           s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
     }
@@ -248,13 +263,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     // c > 0, so a fully masked row gives cand = -inf and never grows m_run
     const float cand = mx * c;
 
-    // move the reference maximum only when it is exceeded by the slack.
-    // Every row sees key 0 in the first tile, so m_run is finite from then on
-    // (on the first tile alpha = 2^-inf = 0 clears the empty accumulators).
+    // move the reference maximum only when it is exceeded by the slack. A
+    // row's m_run stays -inf until a tile shows it a key (the first tile
+    // always does without a lower window bound); alpha = 2^-inf = 0 then
+    // clears its still empty accumulators.
     const bool grow = cand > m_run + kRescaleSlack;
     if (__any(grow)) {
       const float m_new = fmaxf(m_run, cand);
-      const float alpha = fast_exp2(m_run - m_new);
+      // a row whose maximum does not move keeps its scale (this also covers
+      // a row that has seen no key yet: -inf - -inf would give NaN)
+      const float alpha = m_new > m_run ? fast_exp2(m_run - m_new) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < kDB; ++i)
@@ -264,14 +282,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     }
 
     // probabilities p = 2^(c*s - m) (masked scores: 2^-inf = 0), summed in
-    // fp32 (lse keeps fp32 accuracy) and packed to bf16 for P.V
+    // fp32 (lse keeps fp32 accuracy) and packed to bf16 for P.V. A row that
+    // has seen no key yet has only masked scores here: subtract 0, not -inf.
+    const float m_sub = m_run == -INFINITY ? 0.0f : m_run;
     float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const float e0 = fast_exp2(__builtin_fmaf(s[kb][2 * r], c, -m_run));
-        const float e1 = fast_exp2(__builtin_fmaf(s[kb][2 * r + 1], c, -m_run));
+        const float e0 = fast_exp2(__builtin_fmaf(s[kb][2 * r], c, -m_sub));
+        const float e1 = fast_exp2(__builtin_fmaf(s[kb][2 * r + 1], c, -m_sub));
         ls0 += e0;
         ls1 += e1;
         pk[kb][r] = pack_bf16x2(e0, e1);
@@ -283,26 +303,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   // ---- tiles. K and V of tile t+1 load while tile t is computed: one
   // barrier per tile, after which tile t is in LDS for every wave and every
   // wave is done with tile t-1, whose stage the loads of tile t+1 overwrite.
-  // Even tiles use stage 0 (k0, v0), odd tiles stage 1 (k1, v1).
+  // Tiles t_first, t_first+2, ... use stage 0 (k0, v0), the others stage 1.
   auto step = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
                   unsigned char* vn) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) {
+    if (t + 1 < t_end) {
       fill_tile(kg, t + 1, kn, fk);
       fill_tile(vg, t + 1, vn, fv);
     }
-    if (t < wtiles) {
+    if (t >= wt_first && t < wt_end) {
       qk(kc);
       softmax(t);
       pv(vc);
     }
   };
-  fill_tile(kg, 0, k0, fk);
-  fill_tile(vg, 0, v0, fv);
-  for (int t = 0; t < ntiles; t += 2) {
+  fill_tile(kg, t_first, k0, fk);
+  fill_tile(vg, t_first, v0, fv);
+  for (int t = t_first; t < t_end; t += 2) {
     step(t, k0, v0, k1, v1);
-    if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
+    if (t + 1 < t_end) step(t + 1, k1, v1, k0, v0);
   }
 
   // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2
@@ -349,6 +369,8 @@ hipError_t launch_typed(const FwdArgs& a) {
   // c is kept positive: a zero or denormal scale is raised to 1e-30, which
   // changes no score by more than 1e-27 and keeps c * (-inf) = -inf
   p.c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+  p.wl = a.wl < 0 ? kUnbounded : a.wl;
+  p.wr = a.wr < 0 ? kUnbounded : a.wr;
   p.negate_q = a.scale < 0.0f;
   p.xcd_remap = (p.BH / p.group) % 8 == 0;
   dim3 grid((unsigned)((long long)p.BH * p.nqb));
@@ -360,9 +382,9 @@ hipError_t launch_typed(const FwdArgs& a) {
 template <typename TIn, typename TOut>
 hipError_t launch_dtype(const FwdArgs& a) {
   if (a.d == 64) {
-    return a.causal ? launch_typed<64, true, TIn, TOut>(a) : launch_typed<64, false, TIn, TOut>(a);
+    return a.masked() ? launch_typed<64, true, TIn, TOut>(a) : launch_typed<64, false, TIn, TOut>(a);
   }
-  return a.causal ? launch_typed<128, true, TIn, TOut>(a) : launch_typed<128, false, TIn, TOut>(a);
+  return a.masked() ? launch_typed<128, true, TIn, TOut>(a) : launch_typed<128, false, TIn, TOut>(a);
 }
 
 }  // namespace

@@ -15,9 +15,10 @@ struct FwdArgs {
   float* lse;
   int B, H, N, d;
   float scale;
-  int causal;
+  int wl, wr;  // key j visible to query i iff i-wl <= j <= i+wr; -1: no bound on that side
   hipStream_t stream;
   int Hkv;  // K/V heads; divides H (H: multi-head attention)
+  bool masked() const { return wl >= 0 || wr >= 0; }
 };
 
 struct BwdArgs {
@@ -33,10 +34,15 @@ struct BwdArgs {
   float* drow;  // workspace: D_i = sum_k dO_ik O_ik, then lse_i * log2(e); 2 x [B,H,N] fp32
   int B, H, N, d;
   float scale;
-  int causal;
+  int wl, wr;  // key j visible to query i iff i-wl <= j <= i+wr; -1: no bound on that side
   hipStream_t stream;
   int Hkv;  // K/V heads of k, v, dk, dv; divides H (H: multi-head attention)
+  bool masked() const { return wl >= 0 || wr >= 0; }
 };
+
+// A window bound that never cuts: larger than any distance between a query
+// and a key, small enough that i + kUnbounded and i - kUnbounded stay in int.
+constexpr int kUnbounded = 1 << 30;
 
 hipError_t launch_forward_bf16(const FwdArgs& a);
 hipError_t launch_forward_f32(const FwdArgs& a);

@@ -32,6 +32,8 @@ class Workload:
     dtype: str          # "f32" (fp32 in/out, rounded to bf16 on load) or "bf16"
     seed: int
     Hkv: int = 0        # K/V heads shared by groups of query heads; 0: H (multi-head)
+    window_left: int = -1   # local window (key j visible to query i iff
+    window_right: int = -1  # i-left <= j <= i+right); -1: no bound on that side
 
     @property
     def shape(self):
@@ -61,8 +63,16 @@ GQA_WORKLOADS = [
 ]
 
 
+# Local attention: every query sees itself and the 1023 keys before it
+# (a causal window of 1024 keys).
+WINDOW_WORKLOADS = [
+    Workload("fwdbwd_window1024_b4h16n4096d128", 4, 16, 4096, 128, True, True, "bf16", 7,
+             window_left=1023, window_right=0),
+]
+
+
 def by_name(name: str) -> Workload:
-    for w in WORKLOADS + GQA_WORKLOADS:
+    for w in WORKLOADS + GQA_WORKLOADS + WINDOW_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)

@@ -51,7 +51,7 @@ typedef enum {
     FA_ERR_SHAPE = 2,     /* B, H or N negative, K/V heads not dividing H, or too large */
     FA_ERR_HEADDIM = 3,   /* d not in {64, 128} */
     FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
-    FA_ERR_ARG = 5,       /* causal not 0/1, or scale not finite */
+    FA_ERR_ARG = 5,       /* causal not 0/1, a window bound below -1, or scale not finite */
     FA_ERR_WORKSPACE = 6, /* backward workspace missing or too small */
     FA_ERR_HIP = 7        /* the HIP runtime reported an error at launch */
 } fa_status;
@@ -169,6 +169,39 @@ int fa_backward_grads_gqa(const void* q, const void* k, const void* v, const voi
                           const float* lse, void* dq, void* dk, void* dv,
                           int B, int H, int H_kv, int N, int d, float scale, int causal,
                           const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Local (sliding-window) attention: the pages name local attention only as a
+ * coming variant (nearauto.com FlashAttention-2 article, section
+ * "今後の仕事"; aiunderstanding.org, "Il futuro dell'attenzione flash").
+ * The mask used generalises the causal one: key j is visible to query i iff
+ *     (window_left  < 0 or j >= i - window_left) and
+ *     (window_right < 0 or j <= i + window_right),
+ * -1 meaning no bound on that side. (-1, 0) is the causal mask, (-1, -1) no
+ * mask, (W-1, 0) a causal window of W keys. Bounds below -1 return
+ * FA_ERR_ARG. Every row sees at least its own key whenever both bounds are
+ * >= 0, and key 0 or key N-1 otherwise, so no row is empty. Query tiles and
+ * key tiles that no visible pair touches are skipped, like the tiles above
+ * the diagonal under the causal mask.
+ *
+ * These calls take the grouped K/V heads of the _gqa calls (H_kv = H:
+ * multi-head attention) and otherwise behave as them.
+ */
+int fa_forward_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int H_kv, int N, int d, float scale, int window_left,
+                      int window_right, hipStream_t stream);
+
+int fa_backward_window(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       int B, int H, int H_kv, int N, int d, float scale, int window_left,
+                       int window_right, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+int fa_backward_grads_window(const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv,
+                             int B, int H, int H_kv, int N, int d, float scale, int window_left,
+                             int window_right, const void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);

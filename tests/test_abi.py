@@ -39,7 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_prep",
             "fa_backward_grads", "fa_backward_workspace_size", "fa_strerror",
-            "fa_forward_gqa", "fa_backward_gqa", "fa_backward_grads_gqa"} <= set(names)
+            "fa_forward_gqa", "fa_backward_gqa", "fa_backward_grads_gqa",
+            "fa_forward_window", "fa_backward_window", "fa_backward_grads_window"} <= set(names)
     raw = ctypes.CDLL(fa.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), f"{name} declared in include/ but not exported"
@@ -182,6 +183,38 @@ def test_grouped_validation(lib):
         assert fwd_g(ptrs=ptrs) == FA_ERR_NULL
     assert bwd_g(wb=ws - 1) == FA_ERR_WORKSPACE
     assert grads_g(wb=ws - 1) == FA_ERR_WORKSPACE
+
+
+def test_window_validation(lib):
+    """Window bounds must be >= -1 (-1: none); heads and the rest as for the _gqa calls."""
+    ws = 2 * 4 * 16 * 4
+
+    def fwd_w(wl=3, wr=0, H=4, Hkv=2, ptrs=None, N=16, d=64):
+        ptrs = ptrs or [P] * 5
+        return lib.fa_forward_window(*ptrs, 1, H, Hkv, N, d, 0.125, wl, wr, NULL)
+
+    def bwd_w(wl=3, wr=0, H=4, Hkv=2, ptrs=None, N=16, d=64, wb=ws):
+        ptrs = ptrs or [P] * 9
+        return lib.fa_backward_window(*ptrs, 1, H, Hkv, N, d, 0.125, wl, wr, P, wb, NULL)
+
+    def grads_w(wl=3, wr=0, H=4, Hkv=2, ptrs=None, N=16, d=64, wb=ws):
+        ptrs = ptrs or [P] * 8
+        return lib.fa_backward_grads_window(*ptrs, 1, H, Hkv, N, d, 0.125, wl, wr, P, wb, NULL)
+
+    n_ptrs = {fwd_w: 5, bwd_w: 9, grads_w: 8}
+    for call in (fwd_w, bwd_w, grads_w):
+        for wl, wr in ((-2, 0), (0, -2), (-5, -5)):
+            assert call(wl=wl, wr=wr) == FA_ERR_ARG, (call.__name__, wl, wr)
+        assert call(H=4, Hkv=3) == FA_ERR_SHAPE
+        assert call(d=80) == FA_ERR_HEADDIM
+        ptrs = [P] * n_ptrs[call]
+        ptrs[0] = NULL
+        assert call(ptrs=ptrs) == FA_ERR_NULL
+        ptrs[0] = PM
+        assert call(ptrs=ptrs) == FA_ERR_ALIGN
+        assert call(N=0, ptrs=[NULL] * n_ptrs[call]) == FA_OK
+    assert bwd_w(wb=ws - 4) == FA_ERR_WORKSPACE
+    assert grads_w(wb=ws - 4) == FA_ERR_WORKSPACE
 
 
 def test_python_binding_without_gpu_raises_cleanly(lib):

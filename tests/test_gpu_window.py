@@ -1,0 +1,136 @@
+"""GPU parity of local (sliding-window) attention through the C ABI against the
+fp64 oracle: key j is visible to query i iff i-left <= j <= i+right (-1: no
+bound on that side)."""
+
+from __future__ import annotations
+
+import math
+
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_14_amd import (fa_backward, fa_backward_gqa, fa_backward_grads_window,
+                                   fa_backward_prep, fa_backward_window, fa_forward,
+                                   fa_forward_gqa, fa_forward_window)
+from exact_io_aware_14_amd.inputs import WINDOW_WORKLOADS, draw, to_f64
+from parity import check_grad, check_lse, check_o, log, sample_heads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (B, H, H_kv, N, d): ragged lengths, grouped heads, both head dimensions
+SHAPES = [(1, 2, 2, 300, 64), (1, 4, 2, 513, 128), (2, 2, 1, 200, 128)]
+# (left, right): single key, causal windows below / at / across a 64-key
+# tile, both sides bounded, unbounded left or right, wider than N
+WINDOWS = [(0, 0), (16, 0), (63, 0), (64, 0), (100, 0), (5, 7), (-1, 40), (200, -1),
+           (31, 31), (1000, 1000), (0, 65)]
+
+
+def _ids(cases):
+    return [f"{w[0]},{w[1]}" for w in cases]
+
+
+@pytest.mark.parametrize("window", WINDOWS, ids=_ids(WINDOWS))
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+def test_window_forward(shape, window):
+    B, H, Hkv, N, d = shape
+    q, k, v = draw((B, H, N, d), 500 + N, kv_heads=Hkv)
+    scale = 1.0 / math.sqrt(d)
+    log(f"case window forward {shape} {window}")
+    o, lse = fa_forward_window(q.to(DEV), k.to(DEV), v.to(DEV), *window, scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            g = oracle.kv_head(h, H, Hkv)
+            ro, rl = oracle.forward_head(to_f64(q[b, h]), to_f64(k[b, g]), to_f64(v[b, g]),
+                                         scale, window)
+            check_o(o[b, h], ro, f"{shape} {window} b={b} h={h}")
+            check_lse(lse[b, h], rl, f"{shape} {window} b={b} h={h}")
+
+
+@pytest.mark.parametrize("window", WINDOWS, ids=_ids(WINDOWS))
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+def test_window_backward(shape, window):
+    B, H, Hkv, N, d = shape
+    q, k, v, do = draw((B, H, N, d), 600 + N, with_grad=True, kv_heads=Hkv)
+    scale = 1.0 / math.sqrt(d)
+    log(f"case window backward {shape} {window}")
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa_forward_window(qd, kd, vd, *window, scale=scale)
+    dq, dk, dv = fa_backward_window(qd, kd, vd, o, dod, lse, *window, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, window)
+    dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            check_grad(dq[b, h], rq[b, h], f"{shape} {window} b={b} h={h} dQ")
+        for g in range(Hkv):
+            check_grad(dk[b, g], rk[b, g], f"{shape} {window} b={b} kv={g} dK")
+            check_grad(dv[b, g], rv[b, g], f"{shape} {window} b={b} kv={g} dV")
+
+
+def test_window_causal_and_full_are_the_plain_calls():
+    """(-1, 0) is the causal mask and (-1, -1) none: bitwise the results of the
+    calls without a window."""
+    B, H, Hkv, N, d = 1, 4, 2, 333, 128
+    q, k, v, do = (x.to(DEV) for x in draw((B, H, N, d), 61, with_grad=True, kv_heads=Hkv))
+    for window, causal in (((-1, 0), True), ((-1, -1), False)):
+        o1, l1 = fa_forward_window(q, k, v, *window)
+        o2, l2 = fa_forward_gqa(q, k, v, causal=causal)
+        g1 = fa_backward_window(q, k, v, o1, do, l1, *window)
+        g2 = fa_backward_gqa(q, k, v, o2, do, l2, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
+    # and with all heads distinct, the multi-head calls
+    qm, km, vm, dom = (x.to(DEV) for x in draw((1, 2, 200, 64), 62, with_grad=True))
+    o1, l1 = fa_forward_window(qm, km, vm, -1, 0)
+    o2, l2 = fa_forward(qm, km, vm, causal=True)
+    g1 = fa_backward_window(qm, km, vm, o1, dom, l1, -1, 0)
+    g2 = fa_backward(qm, km, vm, o2, dom, l2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_window_stages_match_backward():
+    B, H, Hkv, N, d = 1, 4, 2, 300, 64
+    q, k, v, do = (x.to(DEV) for x in draw((B, H, N, d), 63, with_grad=True, kv_heads=Hkv))
+    o, lse = fa_forward_window(q, k, v, 70, 5)
+    ref = fa_backward_window(q, k, v, o, do, lse, 70, 5)
+    ws = fa_backward_prep(o, do, lse)
+    got = fa_backward_grads_window(q, k, v, do, lse, ws, 70, 5)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
+def test_window_full_size_workload():
+    """The sliding-window workload at full size: sampled heads of O and one
+    head's gradients against the oracle."""
+    w = WINDOW_WORKLOADS[0]
+    window = (w.window_left, w.window_right)
+    log(f"workload {w.name}")
+    q, k, v, do = draw(w.shape, w.seed, with_grad=True)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa_forward_window(qd, kd, vd, *window, scale=w.scale)
+    dq, dk, dv = fa_backward_window(qd, kd, vd, o, dod, lse, *window, scale=w.scale)
+    torch.cuda.synchronize()
+    for x in (o, dq, dk, dv):
+        assert torch.isfinite(x.float()).all()
+    o = o.float().cpu().numpy()
+    heads = sample_heads(w.B, w.H, 2, seed=w.seed)
+    for b, h in heads:
+        ro, _ = oracle.forward_head(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.scale,
+                                    window)
+        check_o(o[b, h], ro, f"{w.name} b={b} h={h}")
+    b, h = heads[0]
+    rq, rk, rv = oracle.backward_head(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]),
+                                      to_f64(do[b, h]), w.scale, window)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check_grad(got[b, h].float().cpu().numpy(), ref, f"{w.name} b={b} h={h} {name}")
