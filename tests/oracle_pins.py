@@ -29,6 +29,7 @@ import numpy as np
 import torch
 
 import oracle.attention as A
+import oracle.fp8 as F
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_form.json")
 
@@ -424,8 +425,117 @@ def pin_window_brute_force():
             assert abs(lse[i] - math.log(tot)) < 1e-12
 
 
+# ---------------------------------------------------------------- FP8 with incoherent processing
+
+def pin_fp8_e4m3_golden():
+    data = json.load(open(os.path.join(os.path.dirname(GOLDEN), "fp8_e4m3.json")))
+    for case in data["cases"]:
+        got = float(F.e4m3_round(case["x"]))
+        assert got == case["q"], f"e4m3({case['x']}) = {got}, expected {case['q']} ({case['why']})"
+
+
+def pin_fp8_e4m3_grid():
+    vals = F.e4m3_values()
+    assert len(vals) == 127 and vals[-1] == 448.0 and np.all(np.diff(vals) > 0)
+    # every representable value is a fixed point, with either sign
+    assert np.array_equal(F.e4m3_round(vals), vals)
+    assert np.array_equal(F.e4m3_round(-vals), -vals)
+    # a midpoint goes to the neighbour with the even mantissa (grid index even)
+    mids = (vals[:-1] + vals[1:]) / 2
+    want = np.where(np.arange(len(mids)) % 2 == 0, vals[:-1], vals[1:])
+    assert np.array_equal(F.e4m3_round(mids), want)
+    # just inside a midpoint goes to the nearer value
+    eps = np.diff(vals) * 1e-3
+    assert np.array_equal(F.e4m3_round(mids - eps), vals[:-1])
+    assert np.array_equal(F.e4m3_round(mids + eps), vals[1:])
+
+
+def pin_fp8_scales():
+    """Power-of-two scales, worked by hand: the smallest 2^e with max / 2^e <= 448."""
+    got = F.pow2_scale(np.array([448.0, 449.0, 224.0, 224.5, 0.0, 1e-3]))
+    assert np.array_equal(got, [1.0, 2.0, 0.5, 1.0, 1.0, 2.0 ** -18]), got
+    x = np.zeros((130, 8))
+    x[5, 3] = 1000.0          # tile 0: 1000 / 448 = 2.23 -> 4
+    x[74, 0] = -0.5           # tile 1: 0.5 / 448 = 2^-9.81 -> 2^-9
+    x[128:, 1] = 3.0          # tile 2 (ragged, 2 rows): 3 / 448 = 2^-7.22 -> 2^-7
+    codes, b = F.quantize_tiles(x)
+    assert np.array_equal(b, np.repeat([4.0, 2.0 ** -9, 2.0 ** -7], [64, 64, 2]))
+    assert codes[5, 3] == 256.0 and codes[74, 0] == -256.0 and codes[129, 1] == 384.0
+    codes, a = F.quantize_rows(x)
+    assert a[5] == 4.0 and a[74] == 2.0 ** -9 and a[0] == 1.0 and a[129] == 2.0 ** -7
+    assert codes[5, 3] == 256.0
+
+
+def pin_fp8_hadamard():
+    for d in (1, 2, 64, 128):
+        h = F.hadamard(d)
+        assert np.all(np.abs(h) == 1.0)
+        assert np.array_equal(h @ h.T, d * np.eye(d))
+
+
+def pin_fp8_rotation_is_exact():
+    """Without quantisation the random-sign Hadamard changes no score:
+    (Q diag(s) H)(K diag(s) H)^T / d = Q K^T."""
+    rng = np.random.default_rng(41)
+    for n, d in ((40, 64), (70, 128)):
+        q, k, v = _rand_head(rng, n, d)
+        signs = rng.choice([-1.0, 1.0], size=d)
+        s_rot = F.fp8_scores(q, k, 0.3, signs, quantize=False)
+        _close(s_rot, 0.3 * (q @ k.T), 1e-12, f"rotated scores d={d}")
+        o, lse = F.forward_fp8_head(q, k, v, 0.3, True, signs, quantize=False)
+        ro, rl = A.forward_head(q, k, v, 0.3, True)
+        _close(o, ro, 1e-12, f"rotated forward O d={d}")
+        _close(lse, rl, 1e-12, f"rotated forward lse d={d}")
+
+
+def pin_fp8_error_bound():
+    """Each quantised operand is within 2^-4 (relative, normals) plus 2^-10
+    (absolute, subnormals, in units of its scale) of the exact value, so a
+    score errs by at most sum_c |q~_c| |k~_c| (2^-3 + 2^-8) plus the subnormal
+    terms, times scale / d for the rotated form."""
+    rng = np.random.default_rng(42)
+    n, d, scale = 50, 128, 0.2
+    q, k, _ = _rand_head(rng, n, d)
+    for signs in (None, rng.choice([-1.0, 1.0], size=d)):
+        exact = scale * (q @ k.T)
+        got = F.fp8_scores(q, k, scale, signs)
+        if signs is None:
+            qt, kt, rescale = q, k, 1.0
+        else:
+            m = signs[:, None] * F.hadamard(d)
+            qt, kt, rescale = q @ m, k @ m, 1.0 / d
+        _, a = F.quantize_rows(qt)
+        _, b = F.quantize_tiles(kt)
+        sub_q, sub_k = a * 2.0 ** -10, b * 2.0 ** -10
+        bound = scale * rescale * (
+            (np.abs(qt) @ np.abs(kt).T) * (2.0 ** -3 + 2.0 ** -8)
+            + sub_q[:, None] * np.abs(kt).sum(axis=1)[None, :] * 1.07
+            + np.abs(qt).sum(axis=1)[:, None] * sub_k[None, :] * 1.07
+            + d * sub_q[:, None] * sub_k[None, :])
+        assert np.all(np.abs(got - exact) <= bound), f"fp8 score error bound signs={signs is not None}"
+
+
+def pin_fp8_incoherence_lowers_error():
+    """The pages' claim for incoherent processing: with outlier channels the
+    rotated FP8 scores err less than plain FP8 ones (the page reports 2.6x
+    lower error for FlashAttention-3; here at least 1.5x on the scores)."""
+    rng = np.random.default_rng(43)
+    n, d, scale = 256, 128, 128 ** -0.5
+    q, k, _ = _rand_head(rng, n, d)
+    outliers = rng.choice(d, size=4, replace=False)
+    q[:, outliers] *= 30.0
+    k[:, outliers] *= 30.0
+    signs = rng.choice([-1.0, 1.0], size=d)
+    exact = scale * (q @ k.T)
+    err_plain = np.linalg.norm(F.fp8_scores(q, k, scale, None) - exact)
+    err_rot = np.linalg.norm(F.fp8_scores(q, k, scale, signs) - exact)
+    assert err_plain > 1.5 * err_rot, f"plain {err_plain} vs incoherent {err_rot}"
+
+
 ALL_PINS = [pin_golden_forward, pin_golden_backward, pin_vs_torch_sdpa,
             pin_backward_vs_autograd, pin_finite_differences, pin_brute_force,
             pin_online_recurrence, pin_forward_invariants, pin_backward_invariants,
             pin_gqa_vs_autograd, pin_gqa_finite_differences, pin_window_special_cases,
-            pin_window_vs_torch, pin_window_brute_force]
+            pin_window_vs_torch, pin_window_brute_force, pin_fp8_e4m3_golden,
+            pin_fp8_e4m3_grid, pin_fp8_scales, pin_fp8_hadamard, pin_fp8_rotation_is_exact, pin_fp8_error_bound,
+            pin_fp8_incoherence_lowers_error]

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as A
+import oracle.fp8 as F
 from oracle_pins import ALL_PINS
 
 
@@ -113,6 +114,66 @@ def _window_variant(kind):
     return scores
 
 
+def _e4m3_variant(kind):
+    def rnd(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x) if kind == "no_saturation" else np.minimum(np.abs(x), F.E4M3_MAX)
+        _, k = np.frexp(np.where(a > 0, a, 1.0))
+        e = k - 1.0 if kind == "flush_subnormals" else np.maximum(k - 1.0, -6.0)
+        step = np.exp2(e - (2.0 if kind == "two_mantissa_bits" else 3.0))
+        if kind == "ties_away":
+            q = np.floor(a / step + 0.5) * step
+        else:
+            q = np.round(a / step) * step
+        if kind == "flush_subnormals":
+            q = np.where(a < 2.0 ** -6, 0.0, q)
+        if kind != "no_saturation":
+            q = np.minimum(q, F.E4M3_MAX)
+        return np.where(x < 0, -q, q)
+    return rnd
+
+
+def _hadamard_wrong_block(d):
+    h = F._ORIG["hadamard"](d)
+    if d >= 2:
+        h[d // 2:, d // 2:] *= -1.0   # [[H, H], [H, H]]: no longer orthogonal
+    return h
+
+
+def _scale_floor(maxabs):
+    maxabs = np.asarray(maxabs, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(maxabs > 0, maxabs, F.E4M3_MAX) / F.E4M3_MAX))
+    return np.exp2(e)
+
+
+def _tiles_per_row(x, tile=F.KEY_TILE):
+    return F.quantize_rows(x)
+
+
+def _scores_variant(kind):
+    def scores(q, k, scale, signs=None, quantize=True):
+        q = np.asarray(q, dtype=np.float64)
+        k = np.asarray(k, dtype=np.float64)
+        d = q.shape[1]
+        rescale = 1.0
+        if signs is not None:
+            m = np.asarray(signs, dtype=np.float64)[:, None] * F.hadamard(d)
+            if kind == "rotate_q_only":
+                q, rescale = q @ m, 1.0 / d
+            else:
+                q, k = q @ m, k @ m
+                rescale = 1.0 if kind == "no_rescale" else 1.0 / d
+        if not quantize:
+            return scale * rescale * (q @ k.T)
+        q8, a = F.quantize_rows(q)
+        k8, b = F.quantize_tiles(k)
+        if kind == "k_scale_dropped":
+            b = np.ones_like(b)
+        return scale * rescale * (a[:, None] * (q8 @ k8.T) * b[None, :])
+    return scores
+
+
 MUTATIONS = {
     "scale_dropped": ("_scores", _scores_no_scale),
     "causal_mask_flipped": ("_scores", _scores_flipped_mask),
@@ -133,14 +194,27 @@ MUTATIONS = {
     "window_bounds_swapped": ("_scores", _window_variant("swapped")),
     "window_right_bound_one_wide": ("_scores", _window_variant("right_wide")),
 }
+FP8_MUTATIONS = {
+    "e4m3_two_mantissa_bits": ("e4m3_round", _e4m3_variant("two_mantissa_bits")),
+    "e4m3_ties_away_from_zero": ("e4m3_round", _e4m3_variant("ties_away")),
+    "e4m3_flushes_subnormals": ("e4m3_round", _e4m3_variant("flush_subnormals")),
+    "e4m3_no_saturation": ("e4m3_round", _e4m3_variant("no_saturation")),
+    "hadamard_wrong_block": ("hadamard", _hadamard_wrong_block),
+    "fp8_scale_rounds_down": ("pow2_scale", _scale_floor),
+    "fp8_k_scale_per_row": ("quantize_tiles", _tiles_per_row),
+    "fp8_rotation_not_rescaled": ("fp8_scores", _scores_variant("no_rescale")),
+    "fp8_only_q_rotated": ("fp8_scores", _scores_variant("rotate_q_only")),
+    "fp8_k_scale_dropped": ("fp8_scores", _scores_variant("k_scale_dropped")),
+}
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
+@pytest.mark.parametrize("name", sorted(MUTATIONS) + sorted(FP8_MUTATIONS))
 def test_mutation_is_caught(name, monkeypatch):
-    attr, fn = MUTATIONS[name]
+    module, (attr, fn) = (A, MUTATIONS[name]) if name in MUTATIONS else (F, FP8_MUTATIONS[name])
     A._ORIG = {a: getattr(A, a) for a in ("_scores", "_row_softmax_stats", "forward_head",
                                           "backward_head", "backward", "kv_head")}
-    monkeypatch.setattr(A, attr, fn)
+    F._ORIG = {"hadamard": F.hadamard}
+    monkeypatch.setattr(module, attr, fn)
     failed = []
     for pin in ALL_PINS:
         try:
