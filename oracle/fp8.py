@@ -21,9 +21,14 @@ quantisation error. The pages give no more than that; the readings used:
   a_i = 2^ceil(log2(max_c |Q~_ic| / 448)) and each tile t of 64 consecutive
   keys b_t = 2^ceil(log2(max |K~_jc| / 448)) over the tile (1 when the
   maximum is 0); q8 = e4m3(Q~ / a), k8 = e4m3(K~ / b).
-* S_ij = scale / d * a_i * b_t(j) * sum_c q8_ic k8_jc; the softmax, the
-  causal mask, P V (V not quantised) and lse then follow the exact
-  definition (``oracle.attention``).
+* S_ij = scale / d * a_i * b_t(j) * sum_c q8_ic k8_jc; the mask and lse
+  follow the exact definition (``oracle.attention``) on these scores.
+* The second product is FP8 too. V is quantised without a rotation, with a
+  power-of-two scale per column and block of 32 consecutive keys
+  (v8 = e4m3(V / s), same scale rule). The probabilities relative to the row
+  maximum, P_ij = exp(S_ij - max_j S_ij) in (0, 1], are rounded to e4m3 as
+  they are (no scale), and the row sum uses the unrounded P:
+  O_i = sum_j e4m3(P_ij) s_jc v8_jc / sum_j P_ij.
 * Plain FP8 (no incoherent processing, the pages' baseline) is the same with
   M = I, so S_ij = scale * a_i b_t(j) sum_c q8_ic k8_jc.
 """
@@ -35,7 +40,8 @@ import numpy as np
 from . import attention as _att
 
 E4M3_MAX = 448.0
-KEY_TILE = 64
+KEY_TILE = 64   # keys sharing one K scale
+V_BLOCK = 32    # consecutive keys sharing one V scale per column
 
 
 def e4m3_round(x):
@@ -97,6 +103,16 @@ def quantize_tiles(x, tile=KEY_TILE):
     return e4m3_round(x / a[:, None]), a
 
 
+def quantize_key_blocks(x, block=V_BLOCK):
+    """(codes, per-element scales): in every column, each run of `block`
+    consecutive rows shares one scale."""
+    n = x.shape[0]
+    a = np.empty(x.shape)
+    for r0 in range(0, n, block):
+        a[r0:r0 + block] = pow2_scale(np.max(np.abs(x[r0:r0 + block]), axis=0))[None, :]
+    return e4m3_round(x / a), a
+
+
 def fp8_scores(q, k, scale, signs=None, quantize=True):
     """Scaled scores S (N x N) of one head from FP8 operands. signs: the d
     random signs of the incoherent processing, or None for plain FP8.
@@ -117,8 +133,10 @@ def fp8_scores(q, k, scale, signs=None, quantize=True):
 
 
 def forward_fp8_head(q, k, v, scale, causal, signs=None, quantize=True):
-    """(O, lse) of one head with the FP8 scores of ``fp8_scores`` and the exact
-    softmax, mask and P V of ``oracle.attention``."""
+    """(O, lse) of one head: the FP8 scores of ``fp8_scores`` under the mask
+    of ``oracle.attention``, then O = e4m3(P) V~ / rowsum(P) with
+    P = exp(S - rowmax) and V~ the block-quantised V. quantize=False keeps
+    every operand exact (O is then the exact attention output)."""
     s = fp8_scores(q, k, scale, signs, quantize)
     n = s.shape[0]
     left, right = _att.window_bounds(causal)
@@ -129,5 +147,9 @@ def forward_fp8_head(q, k, v, scale, causal, signs=None, quantize=True):
     if right >= 0:
         s = np.where(keys <= rows + right, s, -np.inf)
     lse = _att._row_softmax_stats(s)
-    p = np.exp(s - lse[:, None])
-    return p @ np.asarray(v, dtype=np.float64), lse
+    v = np.asarray(v, dtype=np.float64)
+    if not quantize:
+        return np.exp(s - lse[:, None]) @ v, lse
+    p = np.exp(s - np.max(s, axis=1, keepdims=True))
+    v8, vs = quantize_key_blocks(v)
+    return (e4m3_round(p) @ (v8 * vs)) / np.sum(p, axis=1, keepdims=True), lse

@@ -466,6 +466,54 @@ def pin_fp8_scales():
     assert codes[5, 3] == 256.0
 
 
+def pin_fp8_forward_golden():
+    data = json.load(open(os.path.join(os.path.dirname(GOLDEN), "fp8_forward.json")))
+    for case in data["cases"]:
+        o, lse = F.forward_fp8_head(np.array(case["q"]), np.array(case["k"]), np.array(case["v"]),
+                                    case["scale"], False)
+        _close(o, case["o"], 1e-12, case["name"] + " O")
+        _close(lse, case["lse"], 1e-12, case["name"] + " lse")
+
+
+def pin_fp8_v_blocks():
+    """V scales per column and block of 32 consecutive keys, worked by hand."""
+    x = np.zeros((70, 3))
+    x[3, 0] = 1000.0     # column 0, keys 0-31: 1000 / 448 -> 4
+    x[40, 0] = 0.5       # column 0, keys 32-63: 0.5 / 448 = 2^-9.81 -> 2^-9
+    x[69, 2] = -3.0      # column 2, keys 64-69 (ragged): 3 / 448 -> 2^-7
+    codes, sc = F.quantize_key_blocks(x)
+    assert np.array_equal(sc[:32, 0], np.full(32, 4.0)) and np.array_equal(sc[32:64, 0], np.full(32, 2.0 ** -9))
+    assert np.array_equal(sc[64:, 0], np.ones(6)) and np.array_equal(sc[:, 1], np.ones(70))
+    assert np.array_equal(sc[64:, 2], np.full(6, 2.0 ** -7)) and sc[0, 2] == 1.0
+    assert codes[3, 0] == 256.0 and codes[40, 0] == 256.0 and codes[69, 2] == -384.0
+
+
+def pin_fp8_pv_error_bound():
+    """Given the FP8 scores S, the FP8 second product errs by at most
+    sum_j |e4m3(P_ij) V~_jc - P_ij V_jc| / l_i, bounded term by term with the
+    e4m3 rounding errors: relative 2^-4 (normals), absolute 2^-10 (P below 2^-6)
+    and 2^-10 times the block scale (V)."""
+    rng = np.random.default_rng(44)
+    n, d, scale = 90, 64, 0.125
+    q, k, v = _rand_head(rng, n, d)
+    v[:, 5] *= 40.0
+    for causal in (False, True):
+        s = F.fp8_scores(q, k, scale)
+        if causal:
+            s = np.where(np.tril(np.ones((n, n), dtype=bool)), s, -np.inf)
+        p = np.exp(s - np.max(s, axis=1, keepdims=True))
+        l = np.sum(p, axis=1, keepdims=True)
+        exact = (p @ v) / l
+        _, bs = F.quantize_key_blocks(v)
+        av = np.abs(v)
+        per = (p @ av) * (2.0 ** -3 + 2.0 ** -8) + 2.0 ** -10 * 1.07 * (np.ones_like(p) @ av) \
+            + 1.07 * 2.0 ** -10 * (p @ bs) + 2.0 ** -20 * (np.ones_like(p) @ bs)
+        got, _ = F.forward_fp8_head(q, k, v, scale, causal)
+        err = np.abs(got - exact)
+        assert np.all(err <= per / l), "fp8 P V error bound"
+        assert np.max(err) > 0.0
+
+
 def pin_fp8_hadamard():
     for d in (1, 2, 64, 128):
         h = F.hadamard(d)
@@ -537,5 +585,6 @@ ALL_PINS = [pin_golden_forward, pin_golden_backward, pin_vs_torch_sdpa,
             pin_online_recurrence, pin_forward_invariants, pin_backward_invariants,
             pin_gqa_vs_autograd, pin_gqa_finite_differences, pin_window_special_cases,
             pin_window_vs_torch, pin_window_brute_force, pin_fp8_e4m3_golden,
-            pin_fp8_e4m3_grid, pin_fp8_scales, pin_fp8_hadamard, pin_fp8_rotation_is_exact, pin_fp8_error_bound,
+            pin_fp8_e4m3_grid, pin_fp8_scales, pin_fp8_v_blocks, pin_fp8_forward_golden,
+            pin_fp8_pv_error_bound, pin_fp8_hadamard, pin_fp8_rotation_is_exact, pin_fp8_error_bound,
             pin_fp8_incoherence_lowers_error]

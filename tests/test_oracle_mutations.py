@@ -174,6 +174,29 @@ def _scores_variant(kind):
     return scores
 
 
+def _fp8_forward_variant(kind):
+    def fwd(q, k, v, scale, causal, signs=None, quantize=True):
+        s = F.fp8_scores(q, k, scale, signs, quantize)
+        n = s.shape[0]
+        if causal:
+            s = np.where(np.tril(np.ones((n, n), dtype=bool)), s, -np.inf)
+        lse = A._row_softmax_stats(s)
+        v = np.asarray(v, dtype=np.float64)
+        if not quantize:
+            return np.exp(s - lse[:, None]) @ v, lse
+        p = np.exp(s - np.max(s, axis=1, keepdims=True))
+        v8, vs = F.quantize_key_blocks(v)
+        pq = p if kind == "p_unrounded" else F.e4m3_round(p)
+        vq = v if kind == "v_unrounded" else v8 * vs
+        den = np.sum(pq if kind == "sum_of_rounded" else p, axis=1, keepdims=True)
+        return (pq @ vq) / den, lse
+    return fwd
+
+
+def _v_blocks_of_64(x, block=F.V_BLOCK):
+    return F._ORIG["quantize_key_blocks"](x, 64)
+
+
 MUTATIONS = {
     "scale_dropped": ("_scores", _scores_no_scale),
     "causal_mask_flipped": ("_scores", _scores_flipped_mask),
@@ -205,6 +228,10 @@ FP8_MUTATIONS = {
     "fp8_rotation_not_rescaled": ("fp8_scores", _scores_variant("no_rescale")),
     "fp8_only_q_rotated": ("fp8_scores", _scores_variant("rotate_q_only")),
     "fp8_k_scale_dropped": ("fp8_scores", _scores_variant("k_scale_dropped")),
+    "fp8_p_not_rounded": ("forward_fp8_head", _fp8_forward_variant("p_unrounded")),
+    "fp8_v_not_rounded": ("forward_fp8_head", _fp8_forward_variant("v_unrounded")),
+    "fp8_row_sum_of_rounded_p": ("forward_fp8_head", _fp8_forward_variant("sum_of_rounded")),
+    "fp8_v_blocks_of_64": ("quantize_key_blocks", _v_blocks_of_64),
 }
 
 
@@ -213,7 +240,7 @@ def test_mutation_is_caught(name, monkeypatch):
     module, (attr, fn) = (A, MUTATIONS[name]) if name in MUTATIONS else (F, FP8_MUTATIONS[name])
     A._ORIG = {a: getattr(A, a) for a in ("_scores", "_row_softmax_stats", "forward_head",
                                           "backward_head", "backward", "kv_head")}
-    F._ORIG = {"hadamard": F.hadamard}
+    F._ORIG = {"hadamard": F.hadamard, "quantize_key_blocks": F.quantize_key_blocks}
     monkeypatch.setattr(module, attr, fn)
     failed = []
     for pin in ALL_PINS:
