@@ -25,10 +25,12 @@ quantisation error. The pages give no more than that; the readings used:
   follow the exact definition (``oracle.attention``) on these scores.
 * The second product is FP8 too. V is quantised without a rotation, with a
   power-of-two scale per column and block of 32 consecutive keys
-  (v8 = e4m3(V / s), same scale rule). The probabilities relative to the row
-  maximum, P_ij = exp(S_ij - max_j S_ij) in (0, 1], are rounded to e4m3 as
-  they are (no scale), and the row sum uses the unrounded P:
-  O_i = sum_j e4m3(P_ij) s_jc v8_jc / sum_j P_ij.
+  (v8 = e4m3(V / s), same scale rule). The probabilities are taken relative
+  to the row maximum rounded up to a whole power of two,
+  P_ij = 2^(log2(e) S_ij - m_i) with m_i = ceil(log2(e) max_j S_ij), so that
+  P is in (0, 1] and any power-of-two change of reference rescales P
+  exactly; they are rounded to e4m3 as they are (no scale), and the row sum
+  uses the unrounded P: O_i = sum_j e4m3(P_ij) s_jc v8_jc / sum_j P_ij.
 * Plain FP8 (no incoherent processing, the pages' baseline) is the same with
   M = I, so S_ij = scale * a_i b_t(j) sum_c q8_ic k8_jc.
 """
@@ -135,8 +137,9 @@ def fp8_scores(q, k, scale, signs=None, quantize=True):
 def forward_fp8_head(q, k, v, scale, causal, signs=None, quantize=True):
     """(O, lse) of one head: the FP8 scores of ``fp8_scores`` under the mask
     of ``oracle.attention``, then O = e4m3(P) V~ / rowsum(P) with
-    P = exp(S - rowmax) and V~ the block-quantised V. quantize=False keeps
-    every operand exact (O is then the exact attention output)."""
+    P = 2^(log2(e) S - m), m the row maximum of log2(e) S rounded up to an
+    integer, and V~ the block-quantised V. quantize=False keeps every operand
+    exact (O is then the exact attention output)."""
     s = fp8_scores(q, k, scale, signs, quantize)
     n = s.shape[0]
     left, right = _att.window_bounds(causal)
@@ -150,6 +153,7 @@ def forward_fp8_head(q, k, v, scale, causal, signs=None, quantize=True):
     v = np.asarray(v, dtype=np.float64)
     if not quantize:
         return np.exp(s - lse[:, None]) @ v, lse
-    p = np.exp(s - np.max(s, axis=1, keepdims=True))
+    m = np.ceil(np.max(s, axis=1, keepdims=True) / np.log(2.0))
+    p = np.exp2(s / np.log(2.0) - m)
     v8, vs = quantize_key_blocks(v)
     return (e4m3_round(p) @ (v8 * vs)) / np.sum(p, axis=1, keepdims=True), lse

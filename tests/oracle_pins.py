@@ -501,7 +501,9 @@ def pin_fp8_pv_error_bound():
         s = F.fp8_scores(q, k, scale)
         if causal:
             s = np.where(np.tril(np.ones((n, n), dtype=bool)), s, -np.inf)
-        p = np.exp(s - np.max(s, axis=1, keepdims=True))
+        # the probabilities relative to the row maximum rounded up to a power of two
+        m = np.ceil(np.max(s, axis=1, keepdims=True) / np.log(2.0))
+        p = np.exp2(s / np.log(2.0) - m)
         l = np.sum(p, axis=1, keepdims=True)
         exact = (p @ v) / l
         _, bs = F.quantize_key_blocks(v)

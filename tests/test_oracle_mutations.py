@@ -184,7 +184,11 @@ def _fp8_forward_variant(kind):
         v = np.asarray(v, dtype=np.float64)
         if not quantize:
             return np.exp(s - lse[:, None]) @ v, lse
-        p = np.exp(s - np.max(s, axis=1, keepdims=True))
+        if kind == "exact_max_reference":
+            p = np.exp(s - np.max(s, axis=1, keepdims=True))
+        else:
+            m = np.ceil(np.max(s, axis=1, keepdims=True) / np.log(2.0))
+            p = np.exp2(s / np.log(2.0) - m)
         v8, vs = F.quantize_key_blocks(v)
         pq = p if kind == "p_unrounded" else F.e4m3_round(p)
         vq = v if kind == "v_unrounded" else v8 * vs
@@ -232,6 +236,7 @@ FP8_MUTATIONS = {
     "fp8_v_not_rounded": ("forward_fp8_head", _fp8_forward_variant("v_unrounded")),
     "fp8_row_sum_of_rounded_p": ("forward_fp8_head", _fp8_forward_variant("sum_of_rounded")),
     "fp8_v_blocks_of_64": ("quantize_key_blocks", _v_blocks_of_64),
+    "fp8_p_reference_exact_max": ("forward_fp8_head", _fp8_forward_variant("exact_max_reference")),
 }
 
 
