@@ -29,8 +29,10 @@ quantisation error. The pages give no more than that; the readings used:
   to the row maximum rounded up to a whole power of two,
   P_ij = 2^(log2(e) S_ij - m_i) with m_i = ceil(log2(e) max_j S_ij), so that
   P is in (0, 1] and any power-of-two change of reference rescales P
-  exactly; they are rounded to e4m3 as they are (no scale), and the row sum
-  uses the unrounded P: O_i = sum_j e4m3(P_ij) s_jc v8_jc / sum_j P_ij.
+  exactly. P is rounded with the power-of-two scale the rule above gives its
+  bound 1, 2^-8 (codes e4m3(2^8 P), so the largest probabilities sit at the
+  top of the e4m3 range and subnormals only start below 2^-14), and the row
+  sum uses the unrounded P: O_i = sum_j 2^-8 e4m3(2^8 P_ij) s_jc v8_jc / sum_j P_ij.
 * Plain FP8 (no incoherent processing, the pages' baseline) is the same with
   M = I, so S_ij = scale * a_i b_t(j) sum_c q8_ic k8_jc.
 """
@@ -156,4 +158,5 @@ def forward_fp8_head(q, k, v, scale, causal, signs=None, quantize=True):
     m = np.ceil(np.max(s, axis=1, keepdims=True) / np.log(2.0))
     p = np.exp2(s / np.log(2.0) - m)
     v8, vs = quantize_key_blocks(v)
-    return (e4m3_round(p) @ (v8 * vs)) / np.sum(p, axis=1, keepdims=True), lse
+    ps = pow2_scale(1.0)
+    return (ps * e4m3_round(p / ps) @ (v8 * vs)) / np.sum(p, axis=1, keepdims=True), lse

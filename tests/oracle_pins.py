@@ -490,9 +490,9 @@ def pin_fp8_v_blocks():
 
 def pin_fp8_pv_error_bound():
     """Given the FP8 scores S, the FP8 second product errs by at most
-    sum_j |e4m3(P_ij) V~_jc - P_ij V_jc| / l_i, bounded term by term with the
-    e4m3 rounding errors: relative 2^-4 (normals), absolute 2^-10 (P below 2^-6)
-    and 2^-10 times the block scale (V)."""
+    sum_j |P~_ij V~_jc - P_ij V_jc| / l_i, bounded term by term with the
+    e4m3 rounding errors: relative 2^-4 (normals), absolute 2^-18 (P, rounded
+    with the scale 2^-8, below 2^-14) and 2^-10 times the block scale (V)."""
     rng = np.random.default_rng(44)
     n, d, scale = 90, 64, 0.125
     q, k, v = _rand_head(rng, n, d)
@@ -508,8 +508,8 @@ def pin_fp8_pv_error_bound():
         exact = (p @ v) / l
         _, bs = F.quantize_key_blocks(v)
         av = np.abs(v)
-        per = (p @ av) * (2.0 ** -3 + 2.0 ** -8) + 2.0 ** -10 * 1.07 * (np.ones_like(p) @ av) \
-            + 1.07 * 2.0 ** -10 * (p @ bs) + 2.0 ** -20 * (np.ones_like(p) @ bs)
+        per = (p @ av) * (2.0 ** -3 + 2.0 ** -8) + 2.0 ** -18 * 1.07 * (np.ones_like(p) @ av) \
+            + 1.07 * 2.0 ** -10 * (p @ bs) + 2.0 ** -28 * (np.ones_like(p) @ bs)
         got, _ = F.forward_fp8_head(q, k, v, scale, causal)
         err = np.abs(got - exact)
         assert np.all(err <= per / l), "fp8 P V error bound"

@@ -190,7 +190,12 @@ def _fp8_forward_variant(kind):
             m = np.ceil(np.max(s, axis=1, keepdims=True) / np.log(2.0))
             p = np.exp2(s / np.log(2.0) - m)
         v8, vs = F.quantize_key_blocks(v)
-        pq = p if kind == "p_unrounded" else F.e4m3_round(p)
+        if kind == "p_unrounded":
+            pq = p
+        elif kind == "p_unscaled":
+            pq = F.e4m3_round(p)
+        else:
+            pq = F.e4m3_round(p * 256.0) / 256.0
         vq = v if kind == "v_unrounded" else v8 * vs
         den = np.sum(pq if kind == "sum_of_rounded" else p, axis=1, keepdims=True)
         return (pq @ vq) / den, lse
@@ -236,6 +241,7 @@ FP8_MUTATIONS = {
     "fp8_v_not_rounded": ("forward_fp8_head", _fp8_forward_variant("v_unrounded")),
     "fp8_row_sum_of_rounded_p": ("forward_fp8_head", _fp8_forward_variant("sum_of_rounded")),
     "fp8_v_blocks_of_64": ("quantize_key_blocks", _v_blocks_of_64),
+    "fp8_p_rounded_without_scale": ("forward_fp8_head", _fp8_forward_variant("p_unscaled")),
     "fp8_p_reference_exact_max": ("forward_fp8_head", _fp8_forward_variant("exact_max_reference")),
 }
 
