@@ -16,7 +16,9 @@ import os
 __all__ = ["FAError", "fa_forward", "fa_forward_gqa", "fa_forward_window", "fa_forward_f32",
            "fa_backward", "fa_backward_gqa", "fa_backward_window", "fa_backward_prep",
            "fa_backward_grads", "fa_backward_grads_gqa", "fa_backward_grads_window",
-           "fa_backward_workspace_size", "fa_strerror", "library", "LIB_PATH"]
+           "fa_backward_workspace_size", "fa_forward_fp8", "fa_fp8_prepare",
+           "fa_forward_fp8_prepared", "fa_forward_fp8_workspace_size", "fa_strerror", "library",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -52,10 +54,16 @@ def library():
                 ("fa_backward_window", [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
                                         i, vp, sz, vp]),
                 ("fa_backward_grads_window", [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f,
-                                              i, i, vp, sz, vp])):
+                                              i, i, vp, sz, vp]),
+                ("fa_forward_fp8", [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]),
+                ("fa_fp8_prepare", [vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]),
+                ("fa_forward_fp8_prepared", [vp, sz, vp, vp, i, i, i, i, i, f, i, vp])):
             if hasattr(lib, name):  # an older build without them fails when they are called
                 getattr(lib, name).argtypes = argtypes
                 getattr(lib, name).restype = i
+        if hasattr(lib, "fa_forward_fp8_workspace_size"):
+            lib.fa_forward_fp8_workspace_size.argtypes = [i, i, i, i, i]
+            lib.fa_forward_fp8_workspace_size.restype = sz
         lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
         lib.fa_backward_workspace_size.restype = sz
         lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
@@ -328,3 +336,106 @@ def fa_backward_grads_window(q, k, v, dout, lse, workspace, window_left, window_
     if st != 0:
         raise FAError(st, "fa_backward_grads_window")
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- FP8 forward
+
+def fa_forward_fp8_workspace_size(B: int, H: int, H_kv: int, N: int, d: int) -> int:
+    return int(library().fa_forward_fp8_workspace_size(B, H, H_kv, N, d))
+
+
+def _signs_arg(signs, d):
+    """Host int8 array for the C call (None: no rotation). Values are checked
+    by the library (FA_ERR_ARG unless each is +1 or -1)."""
+    if signs is None:
+        return None, ctypes.c_void_p(0)
+    vals = [int(x) for x in (signs.tolist() if hasattr(signs, "tolist") else signs)]
+    if len(vals) != d:
+        raise ValueError(f"signs: expected {d} values, got {len(vals)}")
+    arr = (ctypes.c_int8 * d)(*[max(-128, min(127, x)) for x in vals])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def _fp8_shapes(q, k, v):
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    Hkv = _kv_heads(q, k)
+    dev = q.device
+    _check(q, "q", torch.bfloat16, (B, H, N, d), dev)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, torch.bfloat16, (B, Hkv, N, d), dev)
+    return (B, H, Hkv, N, d), dev
+
+
+def _fp8_workspace(shape, dev, workspace):
+    torch = _torch()
+    need = fa_forward_fp8_workspace_size(*shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev:
+        raise ValueError("workspace must be on the same device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def fa_fp8_prepare(q, k, v, signs=None, workspace=None, stream=None):
+    """Rotate (signs: d values of +1/-1, or None) and quantise q, k, v to e4m3
+    into the FP8 workspace, returned as a uint8 tensor (layout in fa.h)."""
+    shape, dev = _fp8_shapes(q, k, v)
+    ws, ws_bytes = _fp8_workspace(shape, dev, workspace)
+    keep, sp = _signs_arg(signs, shape[4])
+    st = library().fa_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), sp, *shape, _ptr(ws), ws_bytes,
+                                  _stream(stream))
+    del keep
+    if st != 0:
+        raise FAError(st, "fa_fp8_prepare")
+    return ws
+
+
+def fa_forward_fp8_prepared(workspace, shape, scale=None, causal=False, o=None, lse=None,
+                            stream=None):
+    """Attention from a workspace fa_fp8_prepare filled; shape = (B, H, H_kv, N, d)."""
+    torch = _torch()
+    B, H, Hkv, N, d = (int(x) for x in shape)
+    dev = workspace.device
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check(o, "o", torch.bfloat16, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    scale = d ** -0.5 if scale is None else scale
+    st = library().fa_forward_fp8_prepared(_ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _ptr(o), _ptr(lse), B, H, Hkv, N, d, float(scale),
+                                           int(bool(causal)), _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_forward_fp8_prepared")
+    return o, lse
+
+
+def fa_forward_fp8(q, k, v, signs=None, scale=None, causal=False, o=None, lse=None,
+                   workspace=None, stream=None):
+    """FP8 forward with incoherent processing (see fa_forward_fp8 in fa.h):
+    q [B,H,N,d], k and v [B,H_kv,N,d] bf16; signs: d values of +1/-1 (the
+    random signs of the Hadamard rotation) or None for plain FP8."""
+    torch = _torch()
+    shape, dev = _fp8_shapes(q, k, v)
+    B, H, Hkv, N, d = shape
+    ws, ws_bytes = _fp8_workspace(shape, dev, workspace)
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check(o, "o", torch.bfloat16, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    scale = d ** -0.5 if scale is None else scale
+    keep, sp = _signs_arg(signs, d)
+    st = library().fa_forward_fp8(_ptr(q), _ptr(k), _ptr(v), sp, _ptr(o), _ptr(lse), *shape,
+                                  float(scale), int(bool(causal)), _ptr(ws), ws_bytes,
+                                  _stream(stream))
+    del keep
+    if st != 0:
+        raise FAError(st, "fa_forward_fp8")
+    return o, lse

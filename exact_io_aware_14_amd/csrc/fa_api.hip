@@ -92,6 +92,52 @@ int backward_common(const void* q, const void* k, const void* v, const void* o,
   return fa::launch_backward_grads(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// FP8 calls: the sign vector (host memory, d entries of +1 or -1, or NULL
+// for no rotation) as a bit mask; false if an entry is neither.
+bool sign_mask(const signed char* signs, int d, uint32_t mask[4], int* rotate) {
+  mask[0] = mask[1] = mask[2] = mask[3] = 0;
+  *rotate = signs != nullptr;
+  if (signs == nullptr) return true;
+  for (int j = 0; j < d; ++j) {
+    if (signs[j] == -1) mask[j >> 5] |= 1u << (j & 31);
+    else if (signs[j] != 1) return false;
+  }
+  return true;
+}
+
+int fp8_check(int B, int H, int Hkv, int N, int d, float scale, int wl, int wr, bool* empty) {
+  int st = check_common(B, H, Hkv, N, d, scale, wl, wr, empty);
+  if (st != FA_OK || *empty) return st;
+  if (fa::fp8_prepare_grid_size(B, H, Hkv, N) > kMaxGrid) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+bool fp8_workspace_ok(const void* ws, size_t bytes, int B, int H, int Hkv, int N, int d) {
+  return ws != nullptr && aligned16(ws) && bytes >= fa::fp8_layout(B, H, Hkv, N, d).bytes;
+}
+
+int fp8_prepare(const void* q, const void* k, const void* v, const signed char* signs, int B,
+                int H, int Hkv, int N, int d, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  const void* ptrs[3] = {q, k, v};
+  int st = check_ptrs(ptrs, 3);
+  if (st != FA_OK) return st;
+  fa::Fp8PrepArgs a{q, k, v, {0, 0, 0, 0}, 0, workspace, B, H, Hkv, N, d, stream};
+  if (!sign_mask(signs, d, a.sign_mask, &a.rotate)) return FA_ERR_ARG;
+  if (!fp8_workspace_ok(workspace, workspace_bytes, B, H, Hkv, N, d)) return FA_ERR_WORKSPACE;
+  return fa::launch_fp8_prepare(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fp8_forward(const void* workspace, size_t workspace_bytes, void* o, float* lse, int B, int H,
+                int Hkv, int N, int d, float scale, int wl, int wr, hipStream_t stream) {
+  const void* ptrs[2] = {o, lse};
+  int st = check_ptrs(ptrs, 2);
+  if (st != FA_OK) return st;
+  if (!fp8_workspace_ok(workspace, workspace_bytes, B, H, Hkv, N, d)) return FA_ERR_WORKSPACE;
+  fa::Fp8FwdArgs a{workspace, o, lse, B, H, Hkv, N, d, scale, wl, wr, stream};
+  return fa::launch_forward_fp8(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 // The causal flag of the entry points without a window: 1 is the window
 // (-1, 0), 0 no mask; anything else is FA_ERR_ARG, reported as an invalid
 // bound.
@@ -199,6 +245,46 @@ int fa_backward_grads_window(const void* q, const void* k, const void* v, const 
                       window_right, workspace, workspace_bytes, stream);
 }
 
+size_t fa_forward_fp8_workspace_size(int B, int H, int H_kv, int N, int d) {
+  bool empty = false;
+  if (fp8_check(B, H, H_kv, N, d, 1.0f, -1, -1, &empty) != FA_OK || empty) return 0;
+  return fa::fp8_layout(B, H, H_kv, N, d).bytes;
+}
+
+int fa_fp8_prepare(const void* q, const void* k, const void* v, const signed char* signs, int B,
+                   int H, int H_kv, int N, int d, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  bool empty = false;
+  int st = fp8_check(B, H, H_kv, N, d, 1.0f, -1, -1, &empty);
+  if (st != FA_OK || empty) return st;
+  return fp8_prepare(q, k, v, signs, B, H, H_kv, N, d, workspace, workspace_bytes, stream);
+}
+
+int fa_forward_fp8_prepared(const void* workspace, size_t workspace_bytes, void* o, float* lse,
+                            int B, int H, int H_kv, int N, int d, float scale, int causal,
+                            hipStream_t stream) {
+  bool empty = false;
+  const int wl = causal_left(causal), wr = causal_right(causal);
+  int st = fp8_check(B, H, H_kv, N, d, scale, wl, wr, &empty);
+  if (st != FA_OK || empty) return st;
+  return fp8_forward(workspace, workspace_bytes, o, lse, B, H, H_kv, N, d, scale, wl, wr, stream);
+}
+
+int fa_forward_fp8(const void* q, const void* k, const void* v, const signed char* signs,
+                   void* o, float* lse, int B, int H, int H_kv, int N, int d, float scale,
+                   int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool empty = false;
+  const int wl = causal_left(causal), wr = causal_right(causal);
+  int st = fp8_check(B, H, H_kv, N, d, scale, wl, wr, &empty);
+  if (st != FA_OK || empty) return st;
+  const void* ptrs[2] = {o, lse};
+  st = check_ptrs(ptrs, 2);
+  if (st != FA_OK) return st;
+  st = fp8_prepare(q, k, v, signs, B, H, H_kv, N, d, workspace, workspace_bytes, stream);
+  if (st != FA_OK) return st;
+  return fp8_forward(workspace, workspace_bytes, o, lse, B, H, H_kv, N, d, scale, wl, wr, stream);
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";
@@ -208,8 +294,9 @@ const char* fa_strerror(int status) {
     case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_ARG:
-      return "invalid argument: causal must be 0 or 1, window bounds >= -1, scale finite";
-    case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or too small";
+      return "invalid argument: causal must be 0 or 1, window bounds >= -1, scale finite, "
+             "signs +1 or -1";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
     default: return "unknown status";
   }

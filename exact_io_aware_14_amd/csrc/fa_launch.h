@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -43,6 +44,38 @@ struct BwdArgs {
 // A window bound that never cuts: larger than any distance between a query
 // and a key, small enough that i + kUnbounded and i - kUnbounded stay in int.
 constexpr int kUnbounded = 1 << 30;
+
+// FP8 forward: byte offsets of the workspace regions (each 256-byte
+// aligned) and its total size.
+struct Fp8Layout {
+  size_t q8, qs, k8, ks, v8, vs, bytes;
+};
+Fp8Layout fp8_layout(int B, int H, int Hkv, int N, int d);
+
+struct Fp8PrepArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  uint32_t sign_mask[4];  // bit j set: sign s_j = -1 (used when rotate != 0)
+  int rotate;             // apply diag(s) H to Q and K
+  void* workspace;
+  int B, H, Hkv, N, d;
+  hipStream_t stream;
+};
+
+struct Fp8FwdArgs {
+  const void* workspace;  // filled by the prepare launch with the same shapes
+  void* o;
+  float* lse;
+  int B, H, Hkv, N, d;
+  float scale;
+  int wl, wr;
+  hipStream_t stream;
+};
+
+hipError_t launch_fp8_prepare(const Fp8PrepArgs& a);
+hipError_t launch_forward_fp8(const Fp8FwdArgs& a);
+long long fp8_prepare_grid_size(int B, int H, int Hkv, int N);
 
 hipError_t launch_forward_bf16(const FwdArgs& a);
 hipError_t launch_forward_f32(const FwdArgs& a);

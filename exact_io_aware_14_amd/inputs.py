@@ -99,6 +99,14 @@ def draw(shape, seed, with_grad=False, dtype="bf16", kv_heads=None):
     return tuple(out)
 
 
+def draw_signs(d, seed):
+    """d random signs (+1/-1, int8) for the FP8 path's Hadamard rotation: the
+    method's own random draw, made here so that both sides receive it."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    bits = torch.randint(0, 2, (d,), generator=g, dtype=torch.int8)
+    return (1 - 2 * bits).to(torch.int8)
+
+
 def draw_workload(w: Workload):
     return draw(w.shape, w.seed, with_grad=w.backward, dtype=w.dtype, kv_heads=w.kv_heads)
 

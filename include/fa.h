@@ -51,8 +51,9 @@ typedef enum {
     FA_ERR_SHAPE = 2,     /* B, H or N negative, K/V heads not dividing H, or too large */
     FA_ERR_HEADDIM = 3,   /* d not in {64, 128} */
     FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
-    FA_ERR_ARG = 5,       /* causal not 0/1, a window bound below -1, or scale not finite */
-    FA_ERR_WORKSPACE = 6, /* backward workspace missing or too small */
+    FA_ERR_ARG = 5,       /* causal not 0/1, a window bound below -1, scale not finite,
+                             or an FP8 sign not +1/-1 */
+    FA_ERR_WORKSPACE = 6, /* workspace missing, misaligned or too small */
     FA_ERR_HIP = 7        /* the HIP runtime reported an error at launch */
 } fa_status;
 
@@ -202,6 +203,73 @@ int fa_backward_grads_window(const void* q, const void* k, const void* v, const 
                              int B, int H, int H_kv, int N, int d, float scale, int window_left,
                              int window_right, const void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * FP8 forward with incoherent processing. The pages describe FlashAttention-3
+ * computing in FP8 and multiplying Q and K by a Hadamard transform with
+ * random signs, which spreads outliers over the channels and lowers the
+ * quantisation error ("Flash Attention: بهینه‌سازی مکانیزم توجه در
+ * ترنسفورمرها" (deepfa.ir), FlashAttention 3, section "پردازش ناهمدوس برای
+ * FP8"; unite.ai FlashAttention page, section on FlashAttention-3, items 2
+ * and 3). They give no formulas; the readings implemented:
+ *   - M = diag(s) H, s the caller's random signs, H the d x d Sylvester
+ *     Hadamard matrix (H H^T = d I); Q~ = Q M, K~ = K M, so that
+ *     Q~ K~^T / d = Q K^T. signs == NULL: no rotation (plain FP8).
+ *   - FP8 is OCP e4m3 (largest finite 448, subnormals), rounded to nearest
+ *     even. Scales are powers of two: a_i per query row of Q~, b_t per tile
+ *     of 64 keys of K~, s_{g,c} per column c and block g of 32 keys of V
+ *     (not rotated); each the smallest 2^e with max|x| <= 448 * 2^e
+ *     (1 for an all-zero set), and the codes are e4m3(x / scale).
+ *   - S_ij = scale * a_i b_t(j) (q8_i . k8_j) / d (without the / d when not
+ *     rotated); the mask and lse follow S exactly as in fa_forward.
+ *   - O_i = sum_j e4m3(P_ij) s v8_jc / sum_j P_ij with P_ij = exp(S_ij - max_j S_ij);
+ *     the row sum uses the unrounded P.
+ * Arithmetic: Q~ and K~ in fp32 (butterflies), both products on the fp8
+ * MFMA with fp32 accumulation, softmax in fp32; o is bf16 (nearest even),
+ * lse fp32. Inputs must be finite (a NaN or infinity is not propagated).
+ * Block scales of V below 2^-127 (block maxima below about 2^-118) are
+ * raised to 2^-127.
+ *
+ *   q : [B,H,N,d] bf16; k, v : [B,H_kv,N,d] bf16 (H_kv divides H, as in the
+ *       _gqa calls); o : [B,H,N,d] bf16 output; lse : [B,H,N] fp32 output.
+ *   signs : HOST pointer to d values, each +1 or -1 (anything else:
+ *       FA_ERR_ARG), or NULL. Read during the call only.
+ *   causal : 0 or 1, as in fa_forward.
+ *   workspace : device buffer, 16-byte aligned, of at least
+ *       fa_forward_fp8_workspace_size(B,H,H_kv,N,d) bytes (FA_ERR_WORKSPACE
+ *       otherwise); overwritten.
+ * fa_forward_fp8 = fa_fp8_prepare (rotation and quantisation into the
+ * workspace) followed by fa_forward_fp8_prepared (the attention) on the same
+ * stream; the two stages can also be called separately, e.g. to reuse the
+ * quantised K and V for several calls (prepare quantises Q too).
+ *
+ * Workspace layout (byte offsets, every region starting on a multiple of 256
+ * bytes, in this order; T = ceil(N / 64), e4m3 codes as bytes):
+ *   q8 : [B,H,N,d] codes of Q~ / a_i, row-major;
+ *   qs : [B,H,N] fp32 row factors, a_i / d (a_i without rotation);
+ *   k8 : [B,H_kv,T] tiles of 64*d bytes: the code of key 64t+r, column c at
+ *        r*d + 16*((c/16) ^ sk(r)) + c%16, with sk(r) = ((r>>1)&3)|((r>>2)&4)
+ *        for d = 128 and ((r>>2)&1)|((r>>3)&2) for d = 64 (keys past N: 0);
+ *   ks : [B,H_kv,T] fp32 tile scales b_t;
+ *   v8 : [B,H_kv,T] tiles of 64*d bytes holding V^T: the code of key 64t+j,
+ *        column c at c*64 + 16*((j/16) ^ ((c>>2)&3)) + j%16 (keys past N: 0);
+ *   vs : [B,H_kv,T] blocks of 256 bytes: the scale of column c, keys
+ *        64t+32g .. +31 as the byte 127 + e (scale 2^e) at 4*(32g + c%32) + c/32
+ *        (for d = 64 the bytes with c/32 >= 2 are unused).
+ */
+size_t fa_forward_fp8_workspace_size(int B, int H, int H_kv, int N, int d);
+
+int fa_forward_fp8(const void* q, const void* k, const void* v, const signed char* signs,
+                   void* o, float* lse, int B, int H, int H_kv, int N, int d, float scale,
+                   int causal, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int fa_fp8_prepare(const void* q, const void* k, const void* v, const signed char* signs,
+                   int B, int H, int H_kv, int N, int d, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+int fa_forward_fp8_prepared(const void* workspace, size_t workspace_bytes, void* o, float* lse,
+                            int B, int H, int H_kv, int N, int d, float scale, int causal,
+                            hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);

@@ -40,7 +40,9 @@ def test_every_declared_symbol_is_exported(lib):
     assert {"fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_prep",
             "fa_backward_grads", "fa_backward_workspace_size", "fa_strerror",
             "fa_forward_gqa", "fa_backward_gqa", "fa_backward_grads_gqa",
-            "fa_forward_window", "fa_backward_window", "fa_backward_grads_window"} <= set(names)
+            "fa_forward_window", "fa_backward_window", "fa_backward_grads_window",
+            "fa_forward_fp8", "fa_fp8_prepare", "fa_forward_fp8_prepared",
+            "fa_forward_fp8_workspace_size"} <= set(names)
     raw = ctypes.CDLL(fa.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), f"{name} declared in include/ but not exported"
@@ -215,6 +217,62 @@ def test_window_validation(lib):
         assert call(N=0, ptrs=[NULL] * n_ptrs[call]) == FA_OK
     assert bwd_w(wb=ws - 4) == FA_ERR_WORKSPACE
     assert grads_w(wb=ws - 4) == FA_ERR_WORKSPACE
+
+
+def test_fp8_workspace_size(lib):
+    """Regions q8, qs, k8, ks, v8, vs, each rounded up to 256 bytes (T = ceil(N/64))."""
+    # B=1, H=2, H_kv=1, N=100, d=64: 12800 + 1024 + 8192 + 256 + 8192 + 512
+    assert fa.fa_forward_fp8_workspace_size(1, 2, 1, 100, 64) == 30976
+    # B=4, H=16, N=4096, d=128: 32 MiB of each code region, 1 MiB of row factors,
+    # 4*16*64 tile scales, 4*16*64 blocks of 256 B of block scales
+    T = 64
+    want = 2 ** 25 + 4 * 16 * 4096 * 4 + 2 ** 25 + 4 * 16 * T * 4 + 2 ** 25 + 4 * 16 * T * 256
+    assert fa.fa_forward_fp8_workspace_size(4, 16, 16, 4096, 128) == want
+    assert fa.fa_forward_fp8_workspace_size(0, 2, 1, 100, 64) == 0
+    assert fa.fa_forward_fp8_workspace_size(1, 2, 3, 100, 64) == 0
+    assert fa.fa_forward_fp8_workspace_size(1, 2, 1, 100, 96) == 0
+
+
+def test_fp8_validation(lib):
+    """Signs must be +1/-1 (host array) or NULL; workspace of the documented size;
+    the rest as for the _gqa calls."""
+    ws = fa.fa_forward_fp8_workspace_size(1, 4, 2, 100, 64)
+    good = (ctypes.c_int8 * 64)(*([1, -1] * 32))
+    bad = (ctypes.c_int8 * 64)(*([1] * 63 + [0]))
+    gp, bp = ctypes.cast(good, ctypes.c_void_p), ctypes.cast(bad, ctypes.c_void_p)
+
+    def fwd(signs=gp, H=4, Hkv=2, N=100, d=64, scale=0.125, causal=1, ptrs=None, w=P, wb=ws):
+        ptrs = ptrs or [P] * 5
+        return lib.fa_forward_fp8(ptrs[0], ptrs[1], ptrs[2], signs, ptrs[3], ptrs[4], 1, H, Hkv,
+                                  N, d, scale, causal, w, wb, NULL)
+
+    def prep(signs=gp, H=4, Hkv=2, N=100, d=64, ptrs=None, w=P, wb=ws):
+        ptrs = ptrs or [P] * 3
+        return lib.fa_fp8_prepare(*ptrs, signs, 1, H, Hkv, N, d, w, wb, NULL)
+
+    def attn(H=4, Hkv=2, N=100, d=64, scale=0.125, causal=1, ptrs=None, w=P, wb=ws):
+        ptrs = ptrs or [P] * 2
+        return lib.fa_forward_fp8_prepared(w, wb, ptrs[0], ptrs[1], 1, H, Hkv, N, d, scale,
+                                           causal, NULL)
+
+    assert fwd(signs=bp) == FA_ERR_ARG
+    assert prep(signs=bp) == FA_ERR_ARG
+    for call in (fwd, attn):
+        assert call(causal=2) == FA_ERR_ARG
+        assert call(scale=float("nan")) == FA_ERR_ARG
+    for call, n in ((fwd, 5), (prep, 3), (attn, 2)):
+        assert call(H=4, Hkv=3) == FA_ERR_SHAPE
+        assert call(d=80) == FA_ERR_HEADDIM
+        assert call(w=NULL) == FA_ERR_WORKSPACE
+        assert call(wb=ws - 1) == FA_ERR_WORKSPACE
+        assert call(w=PM) == FA_ERR_WORKSPACE
+        for i in range(n):
+            ptrs = [P] * n
+            ptrs[i] = NULL
+            assert call(ptrs=ptrs) == FA_ERR_NULL, (call.__name__, i)
+            ptrs[i] = PM
+            assert call(ptrs=ptrs) == FA_ERR_ALIGN, (call.__name__, i)
+        assert call(N=0, ptrs=[NULL] * n, w=NULL, wb=0) == FA_OK
 
 
 def test_python_binding_without_gpu_raises_cleanly(lib):
