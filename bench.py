@@ -23,9 +23,15 @@ workload B=4, H=16, N=4096, d=128 with a causal window of 1024 keys (seed
 7) through the _window calls; its FLOP count is 4*d per visible (query,
 key) pair, counted exactly.
 
+A fourth, `fp8`, times the FP8 forward with incoherent processing
+(fa_fp8_prepare, then fa_forward_fp8_prepared) on the causal forward
+workload B=4, H=32, N=4096, d=128 (seed 3, signs drawn from seed 3) next to
+the bf16 forward on the same input; its FLOP count is the forward's, and its
+roofline peak the dense fp8 MFMA rate.
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
                        [--copy-calibration] [--no-gqa] [--gqa-only] [--no-window]
-                       [--window-only]
+                       [--window-only] [--no-fp8] [--fp8-only]
 --copy-calibration first runs a plain device copy of 1 GiB (torch's copy
 kernel), whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic
 counters of the attention kernels in the same profiled run.
@@ -45,13 +51,16 @@ sys.path.insert(0, ROOT)
 
 # MI355X dense bf16 MFMA peak: 256 CUs x 4 SIMDs x 1024 flop/clk x 2.4 GHz.
 PEAK_BF16_TFLOPS = 2516.6
+# dense fp8 MFMA peak: twice the bf16 rate.
+PEAK_FP8_TFLOPS = 5033.2
+FP8_WORKLOAD = "fwd_causal_b4h32n4096d128"
 WORKLOAD = "fwdbwd_causal_b4h16n4096d128"
 GQA_WORKLOAD = "fwdbwd_causal_gqa_b4h32kv8n4096d128"
 WINDOW_WORKLOAD = "fwdbwd_window1024_b4h16n4096d128"
 METRIC = "attention TFLOP/s (fwd, fwd+bwd) bf16 on 1 MI355X; % of MFMA peak"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["exact_io_aware_14_amd/csrc/fa_common.h", "exact_io_aware_14_amd/csrc/fa_fwd.hip",
-                  "exact_io_aware_14_amd/csrc/fa_bwd.hip"]
+                  "exact_io_aware_14_amd/csrc/fa_bwd.hip", "exact_io_aware_14_amd/csrc/fa_fp8.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -194,6 +203,56 @@ def measure_variant(name, steps, warmup):
     return out
 
 
+def measure_fp8(steps, warmup):
+    """The FP8 forward (prepare + attention) and the bf16 forward on the same
+    causal input; HIP events time each launch."""
+    import torch
+
+    import exact_io_aware_14_amd as fa
+    from exact_io_aware_14_amd.inputs import by_name, draw, draw_signs
+
+    w = by_name(FP8_WORKLOAD)
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in draw(w.shape, w.seed))
+    signs = draw_signs(w.d, w.seed)
+    shape = (w.B, w.H, w.H, w.N, w.d)
+    ws = torch.empty(fa.fa_forward_fp8_workspace_size(*shape), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fp8_prepare(q, k, v, signs, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_forward_fp8_prepared(ws, shape, w.scale, w.causal, o, lse, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fa.fa_forward(q, k, v, w.scale, w.causal, o, lse, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    (prep_ms, attn_ms, bf16_ms), _ = time_steps(step, steps, warmup, stream)
+    fwd_f, _ = counted_flops(w)
+    attn = fwd_f / (attn_ms * 1e-3) / 1e12
+    return {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+            "steps": steps,
+            "fwd_tflops": round(fwd_f / ((prep_ms + attn_ms) * 1e-3) / 1e12, 2),
+            "attention_tflops": round(attn, 2),
+            "bf16_fwd_tflops": round(fwd_f / (bf16_ms * 1e-3) / 1e12, 2),
+            "speedup_vs_bf16": round(bf16_ms / (prep_ms + attn_ms), 3),
+            "ms": {"prepare": round(prep_ms, 4), "attention": round(attn_ms, 4),
+                   "bf16_fwd": round(bf16_ms, 4)},
+            "roofline": {"bound": "mfma", "kernel": "fwd_fp8_kernel<128,causal>",
+                         "achieved": round(attn, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(attn / PEAK_FP8_TFLOPS, 4),
+                         "traffic": measured_traffic("fwd_fp8_kernel<128,causal>",
+                                                     kernel_source_hash(), FP8_WORKLOAD),
+                         "avg_launch_ms": round(attn_ms, 4)}}
+
+
 def copy_calibration():
     """A plain device copy of 1 GiB (read 1 GiB, write 1 GiB), run once."""
     import torch
@@ -219,6 +278,9 @@ def main():
     ap.add_argument("--no-window", action="store_true")
     ap.add_argument("--window-only", action="store_true",
                     help="time only the local-window step (for its profile)")
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="time only the FP8 forward (for its profile)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -230,6 +292,9 @@ def main():
     if args.gqa_only:
         print(json.dumps({"gqa": measure_variant(GQA_WORKLOAD, args.steps, args.warmup)}),
               flush=True)
+        return
+    if args.fp8_only:
+        print(json.dumps({"fp8": measure_fp8(args.steps, args.warmup)}), flush=True)
         return
     if args.window_only:
         print(json.dumps({"window": measure_variant(WINDOW_WORKLOAD, args.steps, args.warmup)}),
@@ -331,6 +396,8 @@ def main():
         out["gqa"] = measure_variant(GQA_WORKLOAD, args.steps, args.warmup)
     if not args.no_window:
         out["window"] = measure_variant(WINDOW_WORKLOAD, args.steps, args.warmup)
+    if not args.no_fp8:
+        out["fp8"] = measure_fp8(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
     print(json.dumps(out), flush=True)

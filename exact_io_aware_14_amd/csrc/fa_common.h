@@ -96,9 +96,22 @@ __device__ __forceinline__ uint4 negate8(uint4 u) {
   return u;
 }
 
-// Value from the lane 32 positions away (the other half of the wave).
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+// Maximum and sum of x over lanes l and l ^ 32 (the two halves of the
+// wave), in every lane. v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second; with x in both, lane l of
+// the results holds (x[l], x[l+32]) in the lower half and (x[l-32], x[l]) in
+// the upper half: the low-half value first in both, so the two halves add in
+// the same order and agree bitwise.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -104,6 +104,12 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return (uint32_t)cvt_e4m3x2<true>(c, d, cvt_e4m3x2<false>(a, b, 0));
 }
 
+// The same for values known to lie in [0, 448] (the probabilities): no clamp.
+__device__ __forceinline__ uint32_t pack_e4m3x4_unclamped(float a, float b, float c, float d) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false),
+                                                   true);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -475,7 +481,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void fwd_fp8_kernel(Fp8Params p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = halves_max(mx);
     const float cand = mx * ct;
     const bool grow = cand > m_run + kSlack;
     if (__any(grow)) {
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void fwd_fp8_kernel(Fp8Params p) {
         const float e3 = fast_exp2(__builtin_fmaf(s[kb][4 * i + 3], ct, -m_sub));
         ls0 += e0 + e2;
         ls1 += e1 + e3;
-        pk[4 * kb + i] = (int)pack_e4m3x4(e0, e1, e2, e3);
+        pk[4 * kb + i] = (int)pack_e4m3x4_unclamped(e0, e1, e2, e3);  // p <= 2^8
       }
     l_run += ls0 + ls1;
   };
@@ -534,7 +540,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void fwd_fp8_kernel(Fp8Params p) {
   }
 
   // ---- epilogue: O = O_acc / l, lse = (m - kShift + log2 l) ln 2
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (myq < N) {
     uint16_t* og = reinterpret_cast<uint16_t*>(p.o) + (size_t)bh * N * D + (size_t)myq * D;

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kThreads, D == 64 && sizeof(TIn) == 2 ? 4 : 2) void
     for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = halves_max(mx);
     // c > 0, so a fully masked row gives cand = -inf and never grows m_run
     const float cand = mx * c;
 
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kThreads, D == 64 && sizeof(TIn) == 2 ? 4 : 2) void
   }
 
   // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (myq < N) {
     TOut* og = reinterpret_cast<TOut*>(p.o) + head_off + (size_t)myq * D;
