@@ -23,6 +23,10 @@ workload B=4, H=16, N=4096, d=128 with a causal window of 1024 keys (seed
 7) through the _window calls; its FLOP count is 4*d per visible (query,
 key) pair, counted exactly.
 
+A fifth, `d256`, times the forward+backward step at head dimension 256:
+B=4, H=8, N=4096, d=256, causal (seed 8), through the _gqa calls with
+H_kv = H.
+
 A fourth, `fp8`, times the FP8 forward with incoherent processing
 (fa_fp8_prepare, then fa_forward_fp8_prepared) on the causal forward
 workload B=4, H=32, N=4096, d=128 (seed 3, signs drawn from seed 3) next to
@@ -31,7 +35,7 @@ roofline peak the dense fp8 MFMA rate.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
                        [--copy-calibration] [--no-gqa] [--gqa-only] [--no-window]
-                       [--window-only] [--no-fp8] [--fp8-only]
+                       [--window-only] [--no-fp8] [--fp8-only] [--no-d256] [--d256-only]
 --copy-calibration first runs a plain device copy of 1 GiB (torch's copy
 kernel), whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic
 counters of the attention kernels in the same profiled run.
@@ -54,6 +58,7 @@ PEAK_BF16_TFLOPS = 2516.6
 # dense fp8 MFMA peak: twice the bf16 rate.
 PEAK_FP8_TFLOPS = 5033.2
 FP8_WORKLOAD = "fwd_causal_b4h32n4096d128"
+D256_WORKLOAD = "fwdbwd_causal_b4h8n4096d256"
 WORKLOAD = "fwdbwd_causal_b4h16n4096d128"
 GQA_WORKLOAD = "fwdbwd_causal_gqa_b4h32kv8n4096d128"
 WINDOW_WORKLOAD = "fwdbwd_window1024_b4h16n4096d128"
@@ -278,6 +283,9 @@ def main():
     ap.add_argument("--no-window", action="store_true")
     ap.add_argument("--window-only", action="store_true",
                     help="time only the local-window step (for its profile)")
+    ap.add_argument("--no-d256", action="store_true")
+    ap.add_argument("--d256-only", action="store_true",
+                    help="time only the head-dimension-256 step (for its profile)")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--fp8-only", action="store_true",
                     help="time only the FP8 forward (for its profile)")
@@ -291,6 +299,10 @@ def main():
         copy_calibration()
     if args.gqa_only:
         print(json.dumps({"gqa": measure_variant(GQA_WORKLOAD, args.steps, args.warmup)}),
+              flush=True)
+        return
+    if args.d256_only:
+        print(json.dumps({"d256": measure_variant(D256_WORKLOAD, args.steps, args.warmup)}),
               flush=True)
         return
     if args.fp8_only:
@@ -396,6 +408,8 @@ def main():
         out["gqa"] = measure_variant(GQA_WORKLOAD, args.steps, args.warmup)
     if not args.no_window:
         out["window"] = measure_variant(WINDOW_WORKLOAD, args.steps, args.warmup)
+    if not args.no_d256:
+        out["d256"] = measure_variant(D256_WORKLOAD, args.steps, args.warmup)
     if not args.no_fp8:
         out["fp8"] = measure_fp8(args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -19,7 +19,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_common(int B, int H, int Hkv, int N, int d, float scale, int wl, int wr, bool* empty) {
   if (wl < -1 || wr < -1) return FA_ERR_ARG;
   if (!isfinite(scale)) return FA_ERR_ARG;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   // K/V heads: at least one, dividing H (unless there are no heads at all)
   if (Hkv < 0 || (H > 0 && (Hkv == 0 || H % Hkv != 0))) return FA_ERR_SHAPE;
@@ -106,6 +106,7 @@ bool sign_mask(const signed char* signs, int d, uint32_t mask[4], int* rotate) {
 }
 
 int fp8_check(int B, int H, int Hkv, int N, int d, float scale, int wl, int wr, bool* empty) {
+  if (d == 256) return FA_ERR_HEADDIM;  // the FP8 path supports d = 64 and 128
   int st = check_common(B, H, Hkv, N, d, scale, wl, wr, empty);
   if (st != FA_OK || *empty) return st;
   if (fa::fp8_prepare_grid_size(B, H, Hkv, N) > kMaxGrid) return FA_ERR_SHAPE;
@@ -167,7 +168,7 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
 }
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
-  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128 && d != 256)) return 0;
   return 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);  // D and lse * log2(e)
 }
 
@@ -291,7 +292,8 @@ const char* fa_strerror(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE:
       return "invalid shape: B, H or N negative, K/V heads not dividing H, or the problem too large";
-    case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
+    case FA_ERR_HEADDIM:
+      return "unsupported head dimension (supported: 64, 128, 256; the FP8 calls 64, 128)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_ARG:
       return "invalid argument: causal must be 0 or 1, window bounds >= -1, scale finite, "

@@ -158,10 +158,13 @@ __device__ __forceinline__ int tsw(int d) { return (d ^ (d >> 3)) & 7; }
 // separate the rows of (b) while the chunk varies bits 0-1) and bits 0-1
 // from (r >> 2) & 3, completing (a). d = 64 (128-byte rows, r & 1 picks the
 // half of the bank space): bit 2 from (r >> 1) & 1, bits 0-1 from (r >> 2) & 3.
+// d = 256 (512-byte rows, two 256-byte bank spans): the d = 128 swizzle; it
+// changes only the low four bits of a chunk index, so chunk 16 + c of a row
+// sits exactly 256 bytes after chunk c.
 template <int D>
 __device__ __forceinline__ int rsw(int r) {
-  static_assert(D == 64 || D == 128, "tile width");
-  return D == 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+  static_assert(D == 64 || D == 128 || D == 256, "tile width");
+  return D >= 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
 }
 
 // Store chunk `ch` (8 elements) of row `row` into a row-major tile of width D.

@@ -65,7 +65,10 @@ struct FwdParams {
 
 // Workgroup shape: four waves (128 query rows), two workgroups per CU at
 // d = 128 (four at d = 64 with bf16 inputs, at most 128 VGPRs); the waves a SIMD holds belong
-// to different workgroups and overlap freely.
+// to different workgroups and overlap freely. At d = 256 one workgroup per
+// CU: its four LDS stages take 128 KB, and a wave's Q (64 registers) and O
+// accumulators (128) need the SIMD's whole register file (512, accumulators
+// in AGPRs).
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
@@ -78,7 +81,8 @@ struct Layout {
 };
 
 template <int D, int BC, bool CAUSAL, typename TIn, typename TOut>
-__global__ __launch_bounds__(kThreads, D == 64 && sizeof(TIn) == 2 ? 4 : 2) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : (D == 64 && sizeof(TIn) == 2 ? 4 : 2))
+void fwd_kernel(FwdParams p) {
   using LY = Layout<D, BC>;
   // stages 0 and 1 of the K and V tiles (row-major, swizzle rsw)
   __shared__ __attribute__((aligned(1024))) unsigned char k0[LY::kTileBytes];
@@ -88,6 +92,14 @@ __global__ __launch_bounds__(kThreads, D == 64 && sizeof(TIn) == 2 ? 4 : 2) void
   constexpr int kDK = D / 16;   // MFMA steps along d for S^T
   constexpr int kDB = D / 32;   // 32-row blocks of O^T
   constexpr int kKB = BC / 32;  // 32-key blocks of a tile
+  // d = 256: operands are read in chunks (4 steps of S^T, 4 blocks of O^T)
+  // so that the staging registers stay within bounds; per-lane offsets are
+  // kept for the first 128 columns only (kOffDK steps, kOffDB blocks): the
+  // swizzle repeats every 256 bytes of a row (rsw)
+  constexpr int kChK = D == 256 ? 4 : kDK;
+  constexpr int kChB = D == 256 ? 4 : kDB;
+  constexpr int kOffDK = kDK < 8 ? kDK : 8;
+  constexpr int kOffDB = kDB < 4 ? kDB : 4;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,20 +157,22 @@ __global__ __launch_bounds__(kThreads, D == 64 && sizeof(TIn) == 2 ? 4 : 2) void
   }
 
   // ---- per-lane LDS offsets, fixed for the whole loop
-  uint32_t koff[kDK];  // K operand of S^T: row col (+32 kb), chunk 2kk + half
+  uint32_t koff[kOffDK];  // K operand of S^T: row col (+32 kb), chunk 2kk + half
 #pragma unroll
-  for (int kk = 0; kk < kDK; ++kk) koff[kk] = row_offset<D>(col, 2 * kk + half);
-  uint32_t voff[kDB][2];  // V^T operand: d-block db, read 0/1 (+ rows kb*32 + m*16)
+  for (int kk = 0; kk < kOffDK; ++kk) koff[kk] = row_offset<D>(col, 2 * kk + half);
+  uint32_t voff[kOffDB][2];  // V^T operand: d-block db, read 0/1 (+ rows kb*32 + m*16)
 #pragma unroll
-  for (int db = 0; db < kDB; ++db)
+  for (int db = 0; db < kOffDB; ++db)
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) voff[db][rd] = rows_t_offset<D>(db, rd, lane);
-  uint32_t fk[LY::kFill], fv[LY::kFill];  // direct-fill offsets of this lane
+  // offsets of step kk / block db (compile-time constants past the first 128 columns)
+  auto koff_at = [&](int kk) { return koff[kk % kOffDK] + (uint32_t)(kk / kOffDK) * 256u; };
+  auto voff_at = [&](int db, int rd) {
+    return voff[db % kOffDB][rd] + (uint32_t)(db / kOffDB) * 256u;
+  };
+  uint32_t fk[LY::kFill];  // direct-fill offsets of this lane (K and V alike)
 #pragma unroll
-  for (int i = 0; i < LY::kFill; ++i) {
-    fk[i] = fill_lane_offset<D, BC, kWaves>(i, wave, lane);
-    fv[i] = fill_lane_offset<D, BC, kWaves>(i, wave, lane);
-  }
+  for (int i = 0; i < LY::kFill; ++i) fk[i] = fill_lane_offset<D, BC, kWaves>(i, wave, lane);
 
   f32x16 oacc[kDB];
 #pragma unroll
@@ -196,43 +210,51 @@ __global__ __launch_bounds__(kThreads, D == 64 && sizeof(TIn) == 2 ? 4 : 2) void
   // are accumulator rows 8m..8m+7). All operand reads are issued before the
   // first product, so the LDS latency is paid once per half phase.
   auto pv = [&](const unsigned char* vs) {
-    bf16x8 a[kKB][2][kDB];
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
+    for (int c0 = 0; c0 < kDB; c0 += kChB) {
+      bf16x8 a[kKB][2][kChB];
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-        for (int db = 0; db < kDB; ++db)
-          a[kb][m][db] = lds_tr_pair(vs + (kb * 32 + m * 16) * D * 2 + voff[db][0],
-                                     vs + (kb * 32 + m * 16) * D * 2 + voff[db][1]);
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
+          for (int db = 0; db < kChB; ++db)
+            a[kb][m][db] = lds_tr_pair(vs + (kb * 32 + m * 16) * D * 2 + voff_at(c0 + db, 0),
+                                       vs + (kb * 32 + m * 16) * D * 2 + voff_at(c0 + db, 1));
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        uint4 bu = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
-        const bf16x8 b = as_bf16x8(bu);
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-        for (int db = 0; db < kDB; ++db) oacc[db] = mfma32(a[kb][m][db], b, oacc[db]);
-      }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * kKB * kDB, 0);  // the LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kKB * kDB, 0);  // then the MFMAs
+        for (int m = 0; m < 2; ++m) {
+          uint4 bu = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
+          const bf16x8 b = as_bf16x8(bu);
+#pragma unroll
+          for (int db = 0; db < kChB; ++db)
+            oacc[c0 + db] = mfma32(a[kb][m][db], b, oacc[c0 + db]);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * kKB * kChB, 0);  // the LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kKB * kChB, 0);  // then the MFMAs
+    }
   };
 
   // MFMA phase, second half: S^T = K Q^T for the K tile ks
   auto qk = [&](const unsigned char* ks) {
-    bf16x8 a[kDK][kKB];
-#pragma unroll
-    for (int kk = 0; kk < kDK; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) a[kk][kb] = lds_ld16(ks + kb * 32 * D * 2 + koff[kk]);
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) s[kb] = zero16();
 #pragma unroll
-    for (int kk = 0; kk < kDK; ++kk)
+    for (int c0 = 0; c0 < kDK; c0 += kChK) {
+      bf16x8 a[kChK][kKB];
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) s[kb] = mfma32(a[kk][kb], qreg[kk], s[kb]);
-    __builtin_amdgcn_sched_group_barrier(0x100, kDK * kKB, 0);  // the LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, kDK * kKB, 0);  // then the MFMAs
+      for (int kk = 0; kk < kChK; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+          a[kk][kb] = lds_ld16(ks + kb * 32 * D * 2 + koff_at(c0 + kk));
+#pragma unroll
+      for (int kk = 0; kk < kChK; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) s[kb] = mfma32(a[kk][kb], qreg[c0 + kk], s[kb]);
+      __builtin_amdgcn_sched_group_barrier(0x100, kChK * kKB, 0);  // the LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, kChK * kKB, 0);  // then the MFMAs
+    }
   };
 
   // VALU phase: masks, online softmax and P for tile t
@@ -310,7 +332,7 @@ __global__ __launch_bounds__(kThreads, D == 64 && sizeof(TIn) == 2 ? 4 : 2) void
     __syncthreads();
     if (t + 1 < t_end) {
       fill_tile(kg, t + 1, kn, fk);
-      fill_tile(vg, t + 1, vn, fv);
+      fill_tile(vg, t + 1, vn, fk);
     }
     if (t >= wt_first && t < wt_end) {
       qk(kc);
@@ -319,7 +341,7 @@ __global__ __launch_bounds__(kThreads, D == 64 && sizeof(TIn) == 2 ? 4 : 2) void
     }
   };
   fill_tile(kg, t_first, k0, fk);
-  fill_tile(vg, t_first, v0, fv);
+  fill_tile(vg, t_first, v0, fk);
   for (int t = t_first; t < t_end; t += 2) {
     step(t, k0, v0, k1, v1);
     if (t + 1 < t_end) step(t + 1, k1, v1, k0, v0);
@@ -383,6 +405,10 @@ template <typename TIn, typename TOut>
 hipError_t launch_dtype(const FwdArgs& a) {
   if (a.d == 64) {
     return a.masked() ? launch_typed<64, true, TIn, TOut>(a) : launch_typed<64, false, TIn, TOut>(a);
+  }
+  if (a.d == 256) {
+    return a.masked() ? launch_typed<256, true, TIn, TOut>(a)
+                      : launch_typed<256, false, TIn, TOut>(a);
   }
   return a.masked() ? launch_typed<128, true, TIn, TOut>(a) : launch_typed<128, false, TIn, TOut>(a);
 }

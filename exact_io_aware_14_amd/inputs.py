@@ -71,8 +71,15 @@ WINDOW_WORKLOADS = [
 ]
 
 
+# Head dimension 256: the causal forward+backward at the same bytes per
+# tensor as the d = 128 bench workload (half the heads).
+D256_WORKLOADS = [
+    Workload("fwdbwd_causal_b4h8n4096d256", 4, 8, 4096, 256, True, True, "bf16", 8),
+]
+
+
 def by_name(name: str) -> Workload:
-    for w in WORKLOADS + GQA_WORKLOADS + WINDOW_WORKLOADS:
+    for w in WORKLOADS + GQA_WORKLOADS + WINDOW_WORKLOADS + D256_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)

@@ -22,7 +22,8 @@
  * - Heads are independent; query i sees key j iff causal == 0 or j <= i
  *   (equal query and key lengths, lower-triangular mask).
  * - scale is any finite float (callers normally pass 1/sqrt(d)).
- * - Supported head dims: d in {64, 128}. N >= 0, B >= 0, H >= 0, any N
+ * - Supported head dims: d in {64, 128, 256} (the FP8 calls: {64, 128}).
+ *   N >= 0, B >= 0, H >= 0, any N
  *   (a multiple of 128 is the fast case). If B, H or N is 0 the call does
  *   nothing and returns FA_OK; null pointers are then accepted.
  * - Calls are asynchronous: they enqueue kernels on `stream` (NULL means the
@@ -33,7 +34,13 @@
  *   Device faults surface at the caller's next synchronisation.
  * - Sizes: B*H*N*d may exceed 2^31 elements (64-bit offsets between
  *   heads); within one head N*d*4 must be below 2^31 (N < 4194304 at
- *   d = 128), and B*H*ceil(N/128) below 2^31. Otherwise FA_ERR_SHAPE.
+ *   d = 128, N < 2097152 at d = 256), and B*H*ceil(N/128) below 2^31.
+ *   Otherwise FA_ERR_SHAPE.
+ * - Head dim 256 (the nearauto.com FlashAttention-2 article, section
+ *   "新機能", lists head dimensions up to 256 among FlashAttention-2's
+ *   additions) uses the same arithmetic and results as 64 and 128, with
+ *   workgroups of one wave per SIMD (a wave's accumulators need the whole
+ *   register file).
  */
 #ifndef FA_H
 #define FA_H
@@ -49,7 +56,7 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,      /* a required pointer is NULL */
     FA_ERR_SHAPE = 2,     /* B, H or N negative, K/V heads not dividing H, or too large */
-    FA_ERR_HEADDIM = 3,   /* d not in {64, 128} */
+    FA_ERR_HEADDIM = 3,   /* d not in {64, 128, 256} ({64, 128} for the FP8 calls) */
     FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
     FA_ERR_ARG = 5,       /* causal not 0/1, a window bound below -1, scale not finite,
                              or an FP8 sign not +1/-1 */

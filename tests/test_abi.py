@@ -58,6 +58,7 @@ def test_strerror(lib):
 
 def test_workspace_size(lib):
     assert fa.fa_backward_workspace_size(4, 16, 4096, 128) == 2 * 4 * 16 * 4096 * 4
+    assert fa.fa_backward_workspace_size(4, 8, 4096, 256) == 2 * 4 * 8 * 4096 * 4
     assert fa.fa_backward_workspace_size(1, 1, 1, 64) == 8
     assert fa.fa_backward_workspace_size(0, 1, 1, 64) == 0
     assert fa.fa_backward_workspace_size(1, 1, 1, 96) == 0
@@ -89,7 +90,7 @@ def test_forward_validation(lib, f32):
     assert fwd(lib, causal=-1, f32=f32) == FA_ERR_ARG
     assert fwd(lib, scale=float("nan"), f32=f32) == FA_ERR_ARG
     assert fwd(lib, scale=float("inf"), f32=f32) == FA_ERR_ARG
-    for d in (0, 32, 96, 256, -64):
+    for d in (0, 32, 96, 512, -64):
         assert fwd(lib, d=d, f32=f32) == FA_ERR_HEADDIM
     assert fwd(lib, B=-1, f32=f32) == FA_ERR_SHAPE
     assert fwd(lib, H=-2, f32=f32) == FA_ERR_SHAPE
@@ -231,6 +232,7 @@ def test_fp8_workspace_size(lib):
     assert fa.fa_forward_fp8_workspace_size(0, 2, 1, 100, 64) == 0
     assert fa.fa_forward_fp8_workspace_size(1, 2, 3, 100, 64) == 0
     assert fa.fa_forward_fp8_workspace_size(1, 2, 1, 100, 96) == 0
+    assert fa.fa_forward_fp8_workspace_size(1, 2, 1, 100, 256) == 0  # FP8: d = 64 and 128 only
 
 
 def test_fp8_validation(lib):
@@ -263,6 +265,7 @@ def test_fp8_validation(lib):
     for call, n in ((fwd, 5), (prep, 3), (attn, 2)):
         assert call(H=4, Hkv=3) == FA_ERR_SHAPE
         assert call(d=80) == FA_ERR_HEADDIM
+        assert call(d=256) == FA_ERR_HEADDIM
         assert call(w=NULL) == FA_ERR_WORKSPACE
         assert call(wb=ws - 1) == FA_ERR_WORKSPACE
         assert call(w=PM) == FA_ERR_WORKSPACE
