@@ -114,9 +114,9 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const uint16_t* 
 
 // Job of this workgroup in the grads launch. Every K/V head owns nkb dK/dV
 // jobs and group * nqb dQ jobs (those of its query heads). The two kinds
-// are taken alternately while both last, each sequence ordered from the
-// most expensive block down (causal: dK/dV of the first key blocks, dQ of
-// the last query blocks). Consecutive workgroups go to the 8 XCDs in turn;
+// are interleaved evenly, each sequence ordered from the most expensive
+// block down (causal: dK/dV of the first key blocks, dQ of the last query
+// blocks). Consecutive workgroups go to the 8 XCDs in turn;
 // when the head count allows, each XCD gets whole K/V heads (with their
 // query heads) so that their K/V and Q/dO stay in its L2.
 struct Job {
@@ -140,16 +140,17 @@ __device__ __forceinline__ Job job_of(const BwdParams& p) {
     kvh = L % bhkv;
     j = L / bhkv;
   }
-  const int both = p.nkb < ndq ? p.nkb : ndq;
+  // The head's dQ jobs are spread evenly over its slots (slot j is a dQ job
+  // iff floor((j+1) ndq / per_head) > floor(j ndq / per_head)). Within an
+  // XCD, consecutive workgroups go to its four shader engines in turn; an
+  // even spread gives every engine the same mix of the two kinds, where
+  // alternating them left two engines with dK/dV jobs only and workgroups
+  // waiting for them while the other engines had free CUs.
   Job job;
-  int rank;
-  if (j < 2 * both) {
-    job.is_dq = (j & 1) != 0;
-    rank = j >> 1;
-  } else {
-    job.is_dq = ndq > p.nkb;
-    rank = j - both;
-  }
+  const int before = (int)(((long long)j * ndq) / per_head);
+  const int after = (int)(((long long)(j + 1) * ndq) / per_head);
+  job.is_dq = after > before;
+  const int rank = job.is_dq ? before : j - before;
   if (job.is_dq) {
     // rank r: query block r / group (from the last one under the causal
     // mask) of query head r % group of this K/V head
