@@ -142,10 +142,14 @@ __device__ __forceinline__ Job job_of(const BwdParams& p) {
   }
   // The head's dQ jobs are spread evenly over its slots (slot j is a dQ job
   // iff floor((j+1) ndq / per_head) > floor(j ndq / per_head)). Within an
-  // XCD, consecutive workgroups go to its four shader engines in turn; an
-  // even spread gives every engine the same mix of the two kinds, where
-  // alternating them left two engines with dK/dV jobs only and workgroups
-  // waiting for them while the other engines had free CUs.
+  // XCD, consecutive workgroups go to its four shader engines in turn, so
+  // each engine must see the same mix of the two kinds: where one engine
+  // gets only dK/dV jobs, workgroups wait for it while the other engines
+  // have free CUs. The even spread alone alternates the kinds when there
+  // are as many of each (at d = 256), which again splits them by engine;
+  // rotating the slots of each full group of four by the group index gives
+  // every engine both kinds in any case.
+  if ((j | 3) < per_head) j = (j & ~3) | (((j & 3) + (j >> 2)) & 3);
   Job job;
   const int before = (int)(((long long)j * ndq) / per_head);
   const int after = (int)(((long long)(j + 1) * ndq) / per_head);
