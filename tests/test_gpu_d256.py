@@ -12,6 +12,7 @@ import torch
 
 import oracle
 from exact_io_aware_14_amd import (fa_backward, fa_backward_grads, fa_backward_prep,
+                                   fa_backward_workspace_size,
                                    fa_backward_window, fa_forward, fa_forward_f32,
                                    fa_forward_window)
 from exact_io_aware_14_amd.inputs import D256_WORKLOADS, draw, to_f64
@@ -128,3 +129,43 @@ def test_d256_full_size_workload():
                                       to_f64(do[b, h]), w.scale, True)
     for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
         check_grad(got[b, h].float().cpu().numpy(), ref, f"{w.name} b={b} h={h} {name}")
+
+
+def test_d256_writes_every_output_and_is_deterministic():
+    """NaN-poisoned outputs and workspace: every element written, two calls
+    bitwise equal, forward and backward."""
+    shape = (1, 3, 333, D)
+    q, k, v, do = (x.to(DEV) for x in draw(shape, 73, with_grad=True))
+    results = []
+    for _ in range(2):
+        o = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+        fa_forward(q, k, v, causal=True, o=o, lse=lse)
+        grads = [torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+                 for _ in range(3)]
+        ws = torch.full((fa_backward_workspace_size(*shape) // 4,), float("nan"), device=DEV)
+        fa_backward(q, k, v, o, do, lse, causal=True, dq=grads[0], dk=grads[1], dv=grads[2],
+                    workspace=ws)
+        torch.cuda.synchronize()
+        for x in [o, lse] + grads:
+            assert torch.isfinite(x.float()).all()
+        results.append([x.clone() for x in [o, lse] + grads])
+    for a, b in zip(results[0], results[1]):
+        assert torch.equal(a, b)
+
+
+def test_d256_leaves_neighbours_untouched():
+    shape = (1, 2, 200, D)
+    q, k, v, do = (x.to(DEV) for x in draw(shape, 74, with_grad=True))
+    n = int(np.prod(shape))
+    canary = 12288.0
+    bufs = [torch.full((n + 4096,), canary, dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+    lbuf = torch.full((shape[0] * shape[1] * shape[2] + 1024,), canary, device=DEV)
+    o, dq, dk, dv = (b[:n].view(shape) for b in bufs)
+    lse = lbuf[: shape[0] * shape[1] * shape[2]].view(shape[:3])
+    fa_forward(q, k, v, causal=False, o=o, lse=lse)
+    fa_backward(q, k, v, o, do, lse, causal=False, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for b in bufs:
+        assert (b[n:].float() == canary).all()
+    assert (lbuf[lse.numel():] == canary).all()

@@ -255,3 +255,45 @@ def test_fp8_full_size_workload():
         rl = check_fp8_o(o[b, h], to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.scale,
                          True, signs.numpy(), f"{w.name} fp8 b={b} h={h}")
         check_lse(lse[b, h], rl, f"{w.name} fp8 b={b} h={h}")
+
+
+def test_fp8_writes_every_output_and_is_deterministic():
+    """A workspace filled with e4m3 NaN codes (0x7f) and NaN outputs: prepare
+    writes every byte the attention reads (tile padding included), every
+    output is written, and two calls agree bitwise."""
+    for shape, hkv, causal in (((2, 3, 333, 128), 3, True), ((1, 4, 130, 64), 2, False)):
+        B, H, N, d = shape
+        q, k, v = (x.to(DEV) for x in draw(shape, 81, kv_heads=hkv))
+        signs = draw_signs(d, 82)
+        need = fa_forward_fp8_workspace_size(B, H, hkv, N, d)
+        outs = []
+        for _ in range(2):
+            ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)
+            o = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+            lse = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+            fa_forward_fp8(q, k, v, signs, causal=causal, o=o, lse=lse, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+            outs.append((o.clone(), lse.clone()))
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_fp8_leaves_neighbours_untouched():
+    """Nothing is written past o, lse or the workspace's stated size."""
+    shape, hkv = (1, 2, 200, 128), 1
+    B, H, N, d = shape
+    q, k, v = (x.to(DEV) for x in draw(shape, 83, kv_heads=hkv))
+    n = B * H * N * d
+    need = fa_forward_fp8_workspace_size(B, H, hkv, N, d)
+    canary = 12288.0
+    obuf = torch.full((n + 4096,), canary, dtype=torch.bfloat16, device=DEV)
+    lbuf = torch.full((B * H * N + 1024,), canary, device=DEV)
+    wbuf = torch.full((need + 4096,), 0xA5, dtype=torch.uint8, device=DEV)
+    o = obuf[:n].view(shape)
+    lse = lbuf[:B * H * N].view(shape[:3])
+    ws = wbuf[:need]
+    fa_forward_fp8(q, k, v, draw_signs(d, 84), causal=True, o=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    assert (obuf[n:].float() == canary).all()
+    assert (lbuf[B * H * N:] == canary).all()
+    assert (wbuf[need:] == 0xA5).all()
