@@ -60,7 +60,7 @@ def test_backward_small(shape, causal):
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.35])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_backward_scales(scale, d):
     shape = (1, 2, 300, d)
     q, k, v, do = draw(shape, 41, with_grad=True)

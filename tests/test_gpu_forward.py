@@ -59,20 +59,20 @@ def test_forward_small(shape, causal):
 
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.4])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_forward_scales(scale, d):
     _run_and_compare((1, 2, 300, d), True, seed=7, scale=scale)
     _run_and_compare((1, 1, 190, d), False, seed=8, scale=scale)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_forward_peaked_rows(d):
     # Q x 8: sharply peaked softmax rows, the running maximum moves often
     _run_and_compare((1, 2, 700, d), True, seed=9, q_mul=8.0)
     _run_and_compare((1, 2, 700, d), False, seed=10, q_mul=8.0)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_forward_max_moves_every_tile(d):
     # scores grow along the keys: every key tile raises every row maximum,
     # by ~30 in units of log2 per tile
