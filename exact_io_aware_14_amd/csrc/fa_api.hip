@@ -27,6 +27,9 @@ int check_common(int B, int H, int Hkv, int N, int d, float scale, int wl, int w
   if (*empty) return FA_OK;
   // one head of one tensor must be addressable with 32-bit byte offsets
   if ((long long)N * d * (long long)sizeof(float) > kMaxGrid) return FA_ERR_SHAPE;
+  // every head takes at least one workgroup; this also keeps the grid sizes
+  // below from overflowing
+  if ((long long)B * H > kMaxGrid) return FA_ERR_SHAPE;
   if (fa::forward_grid_size(B, H, N) > kMaxGrid) return FA_ERR_SHAPE;
   if (fa::backward_grid_size(B, H, Hkv, N) > kMaxGrid) return FA_ERR_SHAPE;
   return FA_OK;
@@ -168,7 +171,8 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
 }
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
-  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128 && d != 256)) return 0;
+  bool empty = false;
+  if (check_common(B, H, H, N, d, 1.0f, -1, -1, &empty) != FA_OK || empty) return 0;
   return 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);  // D and lse * log2(e)
 }
 

@@ -63,6 +63,10 @@ def test_workspace_size(lib):
     assert fa.fa_backward_workspace_size(0, 1, 1, 64) == 0
     assert fa.fa_backward_workspace_size(1, 1, 1, 96) == 0
     assert fa.fa_backward_workspace_size(1, 1, -5, 64) == 0
+    # shapes the calls reject as too large have no workspace size either
+    assert fa.fa_backward_workspace_size(1 << 30, 1 << 30, 1 << 30, 128) == 0
+    assert fa.fa_backward_workspace_size(1, 1, 1 << 30, 128) == 0
+    assert fa.fa_backward_workspace_size(1 << 30, 1 << 30, 1 << 20, 64) == 0
 
 
 # Fake but aligned device addresses: validation must reject the call before
@@ -97,6 +101,9 @@ def test_forward_validation(lib, f32):
     assert fwd(lib, N=-3, f32=f32) == FA_ERR_SHAPE
     # the grid would not fit a launch
     assert fwd(lib, B=2**20, H=2**10, N=2**16, f32=f32) == FA_ERR_SHAPE
+    # B * H * N past 64 bits: rejected, not wrapped around
+    assert fwd(lib, B=2**30, H=2**30, N=2**20, d=64, f32=f32) == FA_ERR_SHAPE
+    assert fwd(lib, B=2**31 - 1, H=2**31 - 1, N=2**23, d=64, f32=f32) == FA_ERR_SHAPE
     # one head would not be addressable with 32-bit byte offsets
     assert fwd(lib, N=2**22, d=128, f32=f32) == FA_ERR_SHAPE
     for i in range(5):
