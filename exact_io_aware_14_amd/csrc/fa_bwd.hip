@@ -299,7 +299,6 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   const int lo_row = mykey - p.wr, hi_row = mykey + p.wl;  // rows that see this lane's key
   const float c = p.c;
   const unsigned char* kb = smem + LY::kKb + kw * 32 * D * 2;  // this wave's key rows
-  const unsigned char* vb = smem + LY::kVb + kw * 32 * D * 2;
 
   // load tile t of query head jq of the group into LDS stage st
   auto fill = [&](int jq, int t, int st) {
@@ -316,8 +315,11 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   auto tile = [&](int t, int ST, auto mask_c) {
     constexpr bool MASK = decltype(mask_c)::value;
     const int r0 = t * kTile + 32 * qh;  // this wave's first query row
+    // the dO tile lies a fixed distance after the Q tile: one address per
+    // pair of reads, the distance an immediate offset
+    constexpr int kG = LY::kGt - LY::kQt;
+    constexpr int kV = LY::kVb - LY::kKb;
     const unsigned char* qt = smem + LY::kQt + ST * LY::kTileBytes + qh * 32 * D * 2;
-    const unsigned char* gt = smem + LY::kGt + ST * LY::kTileBytes + qh * 32 * D * 2;
     const float* l2t = reinterpret_cast<const float*>(smem + LY::kLv + ST * kTile * 4) + 32 * qh;
     const float* drt = reinterpret_cast<const float*>(smem + LY::kRv + ST * kTile * 4) + 32 * qh;
 
@@ -328,10 +330,12 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
       bf16x8 qa[2], ga[2], ka[2], va[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        qa[u] = lds_ld16(qt + off.row[k2 + u]);
-        ga[u] = lds_ld16(gt + off.row[k2 + u]);
-        ka[u] = lds_ld16(kb + off.row[k2 + u]);
-        va[u] = lds_ld16(vb + off.row[k2 + u]);
+        const unsigned char* qp = qt + off.row[k2 + u];
+        const unsigned char* kp = kb + off.row[k2 + u];
+        qa[u] = lds_ld16(qp);
+        ga[u] = lds_ld16(qp + kG);
+        ka[u] = lds_ld16(kp);
+        va[u] = lds_ld16(kp + kV);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -373,8 +377,10 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
       bf16x8 gta[kDB], qta[kDB];
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        gta[db] = lds_tr_pair(gt + rb + off.tr[db][0], gt + rb + off.tr[db][1]);
-        qta[db] = lds_tr_pair(qt + rb + off.tr[db][0], qt + rb + off.tr[db][1]);
+        const unsigned char* p0 = qt + off.tr[db][0] + rb;
+        const unsigned char* p1 = qt + off.tr[db][1] + rb;
+        gta[db] = lds_tr_pair(p0 + kG, p1 + kG);
+        qta[db] = lds_tr_pair(p0, p1);
       }
       const uint4 pu = {pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]};
       const uint4 du = {dsk[4 * m], dsk[4 * m + 1], dsk[4 * m + 2], dsk[4 * m + 3]};
