@@ -87,6 +87,25 @@ def test_backward_full_size_workload():
     _compare_heads(q, k, v, do, w.scale, w.causal, heads, outs, w.name)
 
 
+def test_backward_long_sequence():
+    """N = 16384, causal, 16 heads (the launch the long-sequence timing uses):
+    one whole head's gradients and sampled rows of its output against the oracle
+    (which holds that head's full 16384 x 16384 matrices in fp64, about 10 GB)."""
+    shape = (1, 16, 16384, 128)
+    scale = 1.0 / math.sqrt(shape[3])
+    q, k, v, do = draw(shape, 47, with_grad=True)
+    log(f"case long sequence {shape}")
+    outs = _fwd_bwd(q, k, v, do, scale, True)
+    for x in outs[2:]:
+        assert torch.isfinite(x.float()).all()
+    h = 11
+    rows = np.concatenate([np.arange(256), np.arange(shape[2] - 256, shape[2])])
+    ro, _ = oracle.forward_head(to_f64(q[0, h]), to_f64(k[0, h]), to_f64(v[0, h]), scale, True,
+                                rows=rows)
+    check_o(outs[0][0, h].float().cpu().numpy()[rows], ro, f"N=16384 h={h}")
+    _compare_heads(q, k, v, do, scale, True, [(0, h)], outs, "N=16384")
+
+
 def test_backward_writes_every_output_and_is_deterministic():
     shape = (2, 2, 333, 128)
     q, k, v, do = (x.to(DEV) for x in draw(shape, 43, with_grad=True))
