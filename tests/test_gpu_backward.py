@@ -87,23 +87,27 @@ def test_backward_full_size_workload():
     _compare_heads(q, k, v, do, w.scale, w.causal, heads, outs, w.name)
 
 
-def test_backward_long_sequence():
-    """N = 16384, causal, 16 heads (the launch the long-sequence timing uses):
-    one whole head's gradients and sampled rows of its output against the oracle
-    (which holds that head's full 16384 x 16384 matrices in fp64, about 10 GB)."""
-    shape = (1, 16, 16384, 128)
+LARGE = [((1, 16, 16384, 128), True, 11), ((2, 16, 4096, 64), False, 13), ((1, 8, 8192, 256), True, 5)]
+
+
+@pytest.mark.parametrize("shape,causal,h", LARGE, ids=[f"{s}-{'c' if c else 'n'}" for s, c, _ in LARGE])
+def test_backward_large_shapes(shape, causal, h):
+    """Long sequences and every head dimension at full launch size: one whole
+    head's gradients and the first and last 256 rows of its output against
+    the oracle (which holds that head's full N x N matrices in fp64: about
+    10 GB at N = 16384)."""
     scale = 1.0 / math.sqrt(shape[3])
-    q, k, v, do = draw(shape, 47, with_grad=True)
-    log(f"case long sequence {shape}")
-    outs = _fwd_bwd(q, k, v, do, scale, True)
+    q, k, v, do = draw(shape, 47 + shape[2] + shape[3], with_grad=True)
+    log(f"case large {shape} causal={causal} head {h}")
+    outs = _fwd_bwd(q, k, v, do, scale, causal)
     for x in outs[2:]:
         assert torch.isfinite(x.float()).all()
-    h = 11
+    b = shape[0] - 1
     rows = np.concatenate([np.arange(256), np.arange(shape[2] - 256, shape[2])])
-    ro, _ = oracle.forward_head(to_f64(q[0, h]), to_f64(k[0, h]), to_f64(v[0, h]), scale, True,
+    ro, _ = oracle.forward_head(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), scale, causal,
                                 rows=rows)
-    check_o(outs[0][0, h].float().cpu().numpy()[rows], ro, f"N=16384 h={h}")
-    _compare_heads(q, k, v, do, scale, True, [(0, h)], outs, "N=16384")
+    check_o(outs[0][b, h].float().cpu().numpy()[rows], ro, f"{shape} b={b} h={h}")
+    _compare_heads(q, k, v, do, scale, causal, [(b, h)], outs, str(shape))
 
 
 def test_backward_writes_every_output_and_is_deterministic():
