@@ -3,9 +3,9 @@
 The functions here carry the names of the C ABI in include/fa.h and only
 marshal arguments: they check torch tensors (device, dtype, contiguity,
 shape), allocate missing outputs with torch, and pass raw device pointers and
-the current HIP stream to the library. Every step of the computation runs in
-the library's HIP kernels; there is no fallback. If libfa.so has not been
-built, every call raises.
+the HIP stream (the one given, else torch's current stream) to the library.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback. If libfa.so has not been built, every call raises.
 """
 
 from __future__ import annotations
@@ -97,11 +97,25 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _stream(stream):
+def _stream(stream, *tensors):
+    """The HIP stream handle of a call: `stream` (a torch stream or a raw
+    handle), else torch's current stream. On any other stream than the
+    current one, the tensors the call reads or writes are recorded on it, so
+    that torch's caching allocator hands their memory to no other work before
+    the call's kernels are done: the binding's own temporaries (outputs and
+    workspaces it allocated) are freed as soon as the caller drops them,
+    possibly while the kernels still run."""
     torch = _torch()
+    current = torch.cuda.current_stream()
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        return ctypes.c_void_p(current.cuda_stream)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if handle != current.cuda_stream:
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(handle)
+        for t in tensors:
+            if t is not None:
+                t.record_stream(s)
+    return ctypes.c_void_p(handle)
 
 
 def _check(t, name, dtype, shape, device):
@@ -142,7 +156,8 @@ def _forward(fn_name, q, k, v, scale, causal, o, lse, stream, dtype, gqa=False, 
     heads = (B, H, Hkv) if gqa else (B, H)
     mask = (int(window[0]), int(window[1])) if window is not None else (int(bool(causal)),)
     st = getattr(library(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                     *heads, N, d, float(scale), *mask, _stream(stream))
+                                     *heads, N, d, float(scale), *mask,
+                                     _stream(stream, q, k, v, o, lse))
     if st != 0:
         raise FAError(st, fn_name)
     return o, lse
@@ -221,7 +236,8 @@ def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=Non
     scale = shape[3] ** -0.5 if scale is None else scale
     st = library().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                _ptr(dq), _ptr(dk), _ptr(dv), *shape, float(scale),
-                               int(bool(causal)), _ptr(ws), ws_bytes, _stream(stream))
+                               int(bool(causal)), _ptr(ws), ws_bytes,
+                               _stream(stream, q, k, v, o, dout, lse, dq, dk, dv, ws))
     if st != 0:
         raise FAError(st, "fa_backward")
     return dq, dk, dv
@@ -232,7 +248,7 @@ def fa_backward_prep(o, dout, lse, workspace=None, stream=None):
     shape, dev, _ = _bwd_check(o, (("o", o), ("dout", dout)), lse, ())
     ws, ws_bytes = _workspace(shape, dev, workspace)
     st = library().fa_backward_prep(_ptr(o), _ptr(dout), _ptr(lse), *shape, _ptr(ws), ws_bytes,
-                                    _stream(stream))
+                                    _stream(stream, o, dout, lse, ws))
     if st != 0:
         raise FAError(st, "fa_backward_prep")
     return ws
@@ -251,7 +267,7 @@ def fa_backward_grads(q, k, v, dout, lse, workspace, scale=None, causal=False, d
                                      _ptr(dq), _ptr(dk), _ptr(dv), *shape, float(scale),
                                      int(bool(causal)), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(),
-                                     _stream(stream))
+                                     _stream(stream, q, k, v, dout, lse, dq, dk, dv, workspace))
     if st != 0:
         raise FAError(st, "fa_backward_grads")
     return dq, dk, dv
@@ -270,7 +286,8 @@ def fa_backward_gqa(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk
     scale = d ** -0.5 if scale is None else scale
     st = library().fa_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                    _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
-                                   int(bool(causal)), _ptr(ws), ws_bytes, _stream(stream))
+                                   int(bool(causal)), _ptr(ws), ws_bytes,
+                                   _stream(stream, q, k, v, o, dout, lse, dq, dk, dv, ws))
     if st != 0:
         raise FAError(st, "fa_backward_gqa")
     return dq, dk, dv
@@ -291,7 +308,8 @@ def fa_backward_grads_gqa(q, k, v, dout, lse, workspace, scale=None, causal=Fals
                                          _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d,
                                          float(scale), int(bool(causal)), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(),
-                                         _stream(stream))
+                                         _stream(stream, q, k, v, dout, lse, dq, dk, dv,
+                                                 workspace))
     if st != 0:
         raise FAError(st, "fa_backward_grads_gqa")
     return dq, dk, dv
@@ -310,7 +328,8 @@ def fa_backward_window(q, k, v, o, dout, lse, window_left, window_right, scale=N
     st = library().fa_backward_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                       _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d,
                                       float(scale), int(window_left), int(window_right),
-                                      _ptr(ws), ws_bytes, _stream(stream))
+                                      _ptr(ws), ws_bytes,
+                                      _stream(stream, q, k, v, o, dout, lse, dq, dk, dv, ws))
     if st != 0:
         raise FAError(st, "fa_backward_window")
     return dq, dk, dv
@@ -332,7 +351,8 @@ def fa_backward_grads_window(q, k, v, dout, lse, workspace, window_left, window_
                                             float(scale), int(window_left), int(window_right),
                                             _ptr(workspace),
                                             workspace.numel() * workspace.element_size(),
-                                            _stream(stream))
+                                            _stream(stream, q, k, v, dout, lse, dq, dk, dv,
+                                                    workspace))
     if st != 0:
         raise FAError(st, "fa_backward_grads_window")
     return dq, dk, dv
@@ -386,7 +406,7 @@ def fa_fp8_prepare(q, k, v, signs=None, workspace=None, stream=None):
     ws, ws_bytes = _fp8_workspace(shape, dev, workspace)
     keep, sp = _signs_arg(signs, shape[4])
     st = library().fa_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), sp, *shape, _ptr(ws), ws_bytes,
-                                  _stream(stream))
+                                  _stream(stream, q, k, v, ws))
     del keep
     if st != 0:
         raise FAError(st, "fa_fp8_prepare")
@@ -409,7 +429,7 @@ def fa_forward_fp8_prepared(workspace, shape, scale=None, causal=False, o=None, 
     st = library().fa_forward_fp8_prepared(_ptr(workspace),
                                            workspace.numel() * workspace.element_size(),
                                            _ptr(o), _ptr(lse), B, H, Hkv, N, d, float(scale),
-                                           int(bool(causal)), _stream(stream))
+                                           int(bool(causal)), _stream(stream, workspace, o, lse))
     if st != 0:
         raise FAError(st, "fa_forward_fp8_prepared")
     return o, lse
@@ -434,7 +454,7 @@ def fa_forward_fp8(q, k, v, signs=None, scale=None, causal=False, o=None, lse=No
     keep, sp = _signs_arg(signs, d)
     st = library().fa_forward_fp8(_ptr(q), _ptr(k), _ptr(v), sp, _ptr(o), _ptr(lse), *shape,
                                   float(scale), int(bool(causal)), _ptr(ws), ws_bytes,
-                                  _stream(stream))
+                                  _stream(stream, q, k, v, o, lse, ws))
     del keep
     if st != 0:
         raise FAError(st, "fa_forward_fp8")

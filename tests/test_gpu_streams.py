@@ -1,0 +1,84 @@
+"""Stream semantics of the C ABI: every call enqueues its kernels on the stream
+it is given (the binding passes torch's current stream when none is named),
+so work queued earlier on that stream is finished first and the results are
+those of the default stream, bitwise."""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+from exact_io_aware_14_amd import (fa_backward, fa_forward, fa_forward_fp8,
+                                   fa_forward_window)
+from exact_io_aware_14_amd.inputs import draw, draw_signs
+from parity import log
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _busy(stream, n=20):
+    """About 20 ms of matrix products queued on `stream`."""
+    with torch.cuda.stream(stream):
+        x = torch.randn(4096, 4096, device=DEV)
+        for _ in range(n):
+            x = torch.tanh(x @ x * 1e-3)
+    return x
+
+
+def test_side_stream_results_equal_default_stream():
+    shape = (2, 4, 333, 128)
+    q, k, v, do = (x.to(DEV) for x in draw(shape, 71, with_grad=True))
+    signs = draw_signs(shape[3], 72)
+    ref_o, ref_lse = fa_forward(q, k, v, causal=True)
+    ref_g = fa_backward(q, k, v, ref_o, do, ref_lse, causal=True)
+    ref_w = fa_forward_window(q, k, v, 40, 3)
+    ref_f = fa_forward_fp8(q, k, v, signs, causal=True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    log("case side stream, current-stream argument")
+    with torch.cuda.stream(s):
+        o, lse = fa_forward(q, k, v, causal=True)
+        g = fa_backward(q, k, v, o, do, lse, causal=True)
+        w = fa_forward_window(q, k, v, 40, 3)
+        f = fa_forward_fp8(q, k, v, signs, causal=True)
+    s.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+    for a, b in zip(g, ref_g):
+        assert torch.equal(a, b)
+    for a, b in zip(w, ref_w):
+        assert torch.equal(a, b)
+    for a, b in zip(f, ref_f):
+        assert torch.equal(a, b)
+
+
+def test_calls_wait_for_earlier_work_on_their_stream():
+    """The inputs are written on a side stream behind ~20 ms of other work and
+    the calls are queued right after on that stream, named explicitly (a torch
+    stream, then the raw handle): if they ran anywhere else they would read the
+    inputs before they are written."""
+    shape = (2, 4, 512, 128)
+    q, k, v, do = (x.to(DEV) for x in draw(shape, 73, with_grad=True))
+    ref_o, ref_lse = fa_forward(q, k, v, causal=True)
+    ref_g = fa_backward(q, k, v, ref_o, do, ref_lse, causal=True)
+    torch.cuda.synchronize()
+
+    q2, do2 = torch.zeros_like(q), torch.zeros_like(do)
+    o = torch.empty_like(q)
+    lse = torch.empty(shape[:3], device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    log("case stream ordering, explicit stream argument")
+    _busy(s)
+    with torch.cuda.stream(s):
+        q2.copy_(q)
+        do2.copy_(do)
+    fa_forward(q2, k, v, causal=True, o=o, lse=lse, stream=s)
+    # a raw stream handle works the same as a torch stream
+    g = fa_backward(q2, k, v, o, do2, lse, causal=True, stream=s.cuda_stream)
+    s.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+    for a, b in zip(g, ref_g):
+        assert torch.equal(a, b)
