@@ -29,6 +29,10 @@
  * - Calls are asynchronous: they enqueue kernels on `stream` (NULL means the
  *   null stream) and return. The library never allocates, frees or
  *   synchronises and keeps no mutable global state, so it is reentrant.
+ *   A call only launches kernels (no allocation, no memset), so it can be
+ *   captured into a HIP graph on `stream` and replayed; a replay reads the
+ *   buffers' contents at replay time. The FP8 sign vector, read from host
+ *   memory during the call, is fixed at capture.
  * - Errors: invalid arguments are reported by a nonzero status BEFORE any
  *   HIP call, and nothing is written. A launch failure returns FA_ERR_HIP.
  *   Device faults surface at the caller's next synchronisation.
