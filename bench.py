@@ -23,15 +23,15 @@ workload B=4, H=16, N=4096, d=128 with a causal window of 1024 keys (seed
 7) through the _window calls; its FLOP count is 4*d per visible (query,
 key) pair, counted exactly.
 
-A fifth, `d256`, times the forward+backward step at head dimension 256:
-B=4, H=8, N=4096, d=256, causal (seed 8), through the _gqa calls with
-H_kv = H.
-
 A fourth, `fp8`, times the FP8 forward with incoherent processing
 (fa_fp8_prepare, then fa_forward_fp8_prepared) on the causal forward
 workload B=4, H=32, N=4096, d=128 (seed 3, signs drawn from seed 3) next to
 the bf16 forward on the same input; its FLOP count is the forward's, and its
 roofline peak the dense fp8 MFMA rate.
+
+A fifth, `d256`, times the forward+backward step at head dimension 256:
+B=4, H=8, N=4096, d=256, causal (seed 8), through the _gqa calls with
+H_kv = H.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
                        [--copy-calibration] [--no-gqa] [--gqa-only] [--no-window]
