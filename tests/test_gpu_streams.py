@@ -82,3 +82,39 @@ def test_calls_wait_for_earlier_work_on_their_stream():
     assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
     for a, b in zip(g, ref_g):
         assert torch.equal(a, b)
+
+
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no mutable global state: forward+backward on two
+    streams at once, on different inputs and shapes, give the sequential
+    results bitwise."""
+    cases = [((2, 4, 700, 128), 74, True), ((1, 8, 513, 64), 75, False)]
+    inputs, refs = [], []
+    for shape, seed, causal in cases:
+        q, k, v, do = (x.to(DEV) for x in draw(shape, seed, with_grad=True))
+        o, lse = fa_forward(q, k, v, causal=causal)
+        g = fa_backward(q, k, v, o, do, lse, causal=causal)
+        inputs.append((q, k, v, do, causal))
+        refs.append((o, lse, *g))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [None, None]
+    log("case two concurrent streams")
+    for _ in range(3):
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        for i, s in enumerate(streams):  # interleave the launches of both streams
+            q, k, v, do, causal = inputs[i]
+            with torch.cuda.stream(s):
+                o, lse = fa_forward(q, k, v, causal=causal)
+                outs[i] = (o, lse)
+        for i, s in enumerate(streams):
+            q, k, v, do, causal = inputs[i]
+            with torch.cuda.stream(s):
+                o, lse = outs[i]
+                outs[i] = (o, lse, *fa_backward(q, k, v, o, do, lse, causal=causal))
+        for s in streams:
+            s.synchronize()
+        for got, ref in zip(outs, refs):
+            for a, b in zip(got, ref):
+                assert torch.equal(a, b)
