@@ -1,0 +1,155 @@
+// Pieces shared by the two sources of the backward pass: fa_bwd.hip (the
+// row-term launch and the grads launch at d = 64 and 128) and fa_bwd_w.hip
+// (the grads launch at d = 256): the job sizes and kernel parameters, the
+// order in which a grads launch hands out its jobs, and the helpers both
+// job kinds use.
+#pragma once
+
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+// d = 64 and 128 job sizes
+constexpr int kKeyBlock = 128;  // keys per dK/dV job
+constexpr int kQBlock = 256;    // query rows per dQ job
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* drow;  // D_i
+  const float* lse2;  // lse_i * log2(e)
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int BH;           // batch * query heads
+  int group;        // query heads per K/V head (1: multi-head attention)
+  int N;
+  int nkb;          // dK/dV jobs (key blocks) per K/V head
+  int nqb;          // dQ jobs (query-row blocks) per query head
+  float c;          // scale * log2(e)
+  float scale;
+  int wl, wr;       // masked kernels: key j visible to query i iff i-wl <= j <= i+wr
+  int xcd_remap;
+};
+
+// d = 256 job sizes
+constexpr int kKeyBlockW = 128;  // keys per dK/dV job
+constexpr int kQBlockW = 128;    // query rows per dQ job
+
+// ---------------------------------------------------------------- layout
+
+// Job of this workgroup in the grads launch. Every K/V head owns nkb dK/dV
+// jobs and group * nqb dQ jobs (those of its query heads). The two kinds
+// are interleaved evenly, each sequence ordered from the most expensive
+// block down (causal: dK/dV of the first key blocks, dQ of the last query
+// blocks). Consecutive workgroups go to the 8 XCDs in turn;
+// when the head count allows, each XCD gets whole K/V heads (with their
+// query heads) so that their K/V and Q/dO stay in its L2.
+struct Job {
+  int bh;    // dK/dV: the K/V head (batch * K/V heads); dQ: the query head
+  int blk;
+  bool is_dq;
+};
+
+template <bool CAUSAL>
+__device__ __forceinline__ Job job_of(const BwdParams& p) {
+  const int L = blockIdx.x;
+  const int ndq = p.group * p.nqb;
+  const int per_head = p.nkb + ndq;
+  const int bhkv = p.BH / p.group;
+  int kvh, j;
+  if (p.xcd_remap) {
+    const int xcd = L & 7, idx = L >> 3;
+    kvh = (idx / per_head) * 8 + xcd;
+    j = idx % per_head;
+  } else {
+    kvh = L % bhkv;
+    j = L / bhkv;
+  }
+  // The head's dQ jobs are spread evenly over its slots (slot j is a dQ job
+  // iff floor((j+1) ndq / per_head) > floor(j ndq / per_head)). Within an
+  // XCD, consecutive workgroups go to its four shader engines in turn, so
+  // each engine must see the same mix of the two kinds: where one engine
+  // gets only dK/dV jobs, workgroups wait for it while the other engines
+  // have free CUs. The even spread alone alternates the kinds when there
+  // are as many of each (at d = 256), which again splits them by engine;
+  // rotating the slots of each full group of four by the group index gives
+  // every engine both kinds in any case.
+  if ((j | 3) < per_head) j = (j & ~3) | (((j & 3) + (j >> 2)) & 3);
+  Job job;
+  const int before = (int)(((long long)j * ndq) / per_head);
+  const int after = (int)(((long long)(j + 1) * ndq) / per_head);
+  job.is_dq = after > before;
+  const int rank = job.is_dq ? before : j - before;
+  if (job.is_dq) {
+    // rank r: query block r / group (from the last one under the causal
+    // mask) of query head r % group of this K/V head
+    const int qbr = rank / p.group;
+    job.bh = kvh * p.group + rank % p.group;
+    job.blk = CAUSAL ? (p.nqb - 1 - qbr) : qbr;
+  } else {
+    job.bh = kvh;
+    job.blk = rank;
+  }
+  return job;
+}
+
+// Start loading 64 floats v[row0 .. row0+63] (zeros past N) into `dst`.
+__device__ __forceinline__ void fill_vec(unsigned char* dst, const float* g, int row0, int N,
+                                         int lane) {
+  const auto r = make_rsrc(g + row0, (uint32_t)(N - row0) * 4u);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)dst, 4, (uint32_t)lane * 4u, 0, 0, 0);
+}
+
+// 32x32 outputs of this lane (column c, 4 groups of 4 rows) as bf16 rows:
+// element r of block db is d = 32*db + 8*(r/4) + 4*half + (r%4).
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16* acc, float sc, int half) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = db * 32 + 8 * g4 + 4 * half;
+      const uint2 w = {pack_bf16x2(acc[db][4 * g4] * sc, acc[db][4 * g4 + 1] * sc),
+                       pack_bf16x2(acc[db][4 * g4 + 2] * sc, acc[db][4 * g4 + 3] * sc)};
+      *reinterpret_cast<uint2*>(dst + d0) = w;
+    }
+}
+
+template <int D>
+BwdParams make_params(const BwdArgs& a) {
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.dout = static_cast<const uint16_t*>(a.dout);
+  p.drow = a.drow;
+  p.lse2 = a.drow + (size_t)a.B * a.H * a.N;
+  p.dq = static_cast<uint16_t*>(a.dq);
+  p.dk = static_cast<uint16_t*>(a.dk);
+  p.dv = static_cast<uint16_t*>(a.dv);
+  p.BH = a.B * a.H;
+  p.group = a.H / a.Hkv;
+  p.N = a.N;
+  const int key_block = D == 256 ? kKeyBlockW : kKeyBlock;
+  const int q_block = D == 256 ? kQBlockW : kQBlock;
+  p.nkb = (a.N + key_block - 1) / key_block;
+  p.nqb = (a.N + q_block - 1) / q_block;
+  p.c = a.scale * kLog2e;
+  p.scale = a.scale;
+  p.wl = a.wl < 0 ? kUnbounded : a.wl;
+  p.wr = a.wr < 0 ? kUnbounded : a.wr;
+  p.xcd_remap = (p.BH / p.group) % 8 == 0;
+  return p;
+}
+
+}  // namespace
+
+// the grads launch at d = 256 (fa_bwd_w.hip)
+hipError_t launch_grads_wide(const BwdArgs& a);
+
+}  // namespace fa
