@@ -192,7 +192,10 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   const int kend = min(k0 + kKeyBlock, N) - 1;
   const int t0 = CAUSAL ? max(0, k0 - p.wr) / kTile : 0;
   const int ntiles = CAUSAL ? min(N - 1, kend + p.wl) / kTile + 1 : (N + kTile - 1) / kTile;
-  const int lo_row = mykey - p.wr, hi_row = mykey + p.wl;  // rows that see this lane's key
+  // rows that see this lane's key: lo_row .. lo_row + n_rows - 1, i.e.
+  // j - wr .. j + wl (the count in unsigned: both bounds may be 2^30)
+  const int lo_row = mykey - p.wr;
+  const uint32_t n_rows = (uint32_t)p.wl + (uint32_t)p.wr + 1u;
   const float c = p.c;
   const unsigned char* kb = smem + LY::kKb + kw * 32 * D * 2;  // this wave's key rows
 
@@ -254,7 +257,7 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
         float pr = fast_exp2(__builtin_fmaf(s[r], c, -l2v[i]));
         if constexpr (MASK) {
           const int row = r0 + rr + i;
-          pr = (row < lo_row || row > hi_row) ? 0.0f : pr;
+          pr = in_window(row, lo_row, n_rows) ? pr : 0.0f;
         }
         pv[i] = pr;
         dsv[i] = pr * (dp[r] - drv[i]);
@@ -417,7 +420,9 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   const int ntiles = CAUSAL ? min(N - 1, qend + p.wr) / kTile + 1 : ntiles_all;
   const int wt0 = CAUSAL ? max(0, qw0 - p.wl) / kTile : 0;
   const int wt1 = qw0 >= N ? wt0 : (CAUSAL ? min(N - 1, wave_last + p.wr) / kTile + 1 : ntiles_all);
-  const int lo_key = myq - p.wl, hi_key = myq + p.wr;  // keys this lane's row sees
+  // keys this lane's row sees: lo_key .. lo_key + n_keys - 1, i.e. i - wl .. i + wr
+  const int lo_key = myq - p.wl;
+  const uint32_t n_keys = (uint32_t)p.wl + (uint32_t)p.wr + 1u;
   const float c = p.c;
 
   auto fill = [&](int t) {
@@ -458,7 +463,7 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
         float pr = fast_exp2(__builtin_fmaf(s[r], c, -l2));
         if constexpr (MASK) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          pr = (key < lo_key || key > hi_key) ? 0.0f : pr;
+          pr = in_window(key, lo_key, n_keys) ? pr : 0.0f;
         }
         dsv[r] = pr * (dp[r] - dr);
       }

@@ -217,6 +217,13 @@ __device__ __forceinline__ void st_tr4(uint16_t* tile, int r0, int ch, const uin
 
 #define FA_LDS __attribute__((address_space(3)))
 
+// Masks with one unsigned compare: x lies in lo .. lo+count-1 iff
+// (unsigned)(x - lo) < count, since values below lo wrap to numbers at least
+// 2^31 (|x - lo| stays below 2^31 for the bounds used here).
+__device__ __forceinline__ bool in_window(int x, int lo, uint32_t count) {
+  return (uint32_t)(x - lo) < count;
+}
+
 // Integer division rounding toward -infinity / +infinity (b > 0).
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
 __device__ __forceinline__ int ceil_div(int a, int b) { return -floor_div(-a, b); }

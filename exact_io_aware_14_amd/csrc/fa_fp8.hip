@@ -359,6 +359,11 @@ __global__ __launch_bounds__(kThreadsF, 2) void fwd_fp8_kernel(Fp8Params p) {
   const int qw0 = q0 + wave * 32;
   const int myq = qw0 + col;
   const int wave_last = min(qw0 + 32, N) - 1;
+  // keys this lane's row sees: lo_key .. lo_key + n_vis - 1 (masked kernels:
+  // i - wl .. i + wr within 0 .. N-1; otherwise 0 .. N-1)
+  const int lo_key = CAUSAL ? myq - p.wl : 0;
+  const int hi_key = CAUSAL ? min(N - 1, myq + p.wr) : N - 1;
+  const uint32_t n_vis = hi_key >= lo_key ? (uint32_t)(hi_key - lo_key + 1) : 0u;
 
   // ---- Q^T (B operand): lane (h, c) holds row myq, d = 64 kk + 32 h .. +31
   i32x8 qreg[kKK];
@@ -472,8 +477,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * kb + 16 * half + r;
-          const bool vis = key < N && (!CAUSAL || (key <= myq + p.wr && key >= myq - p.wl));
-          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+          s[kb][r] = in_window(key, lo_key, n_vis) ? s[kb][r] : -INFINITY;
         }
     }
     float mx = -INFINITY;

@@ -143,6 +143,11 @@ void fwd_kernel(FwdParams p) {
   const int qw0 = q0 + wave * kRowsPerWave;                       // this wave's
   const int myq = qw0 + col;                                      // this lane's row
   const int wave_last = min(qw0 + kRowsPerWave, N) - 1;
+  // keys this lane's row sees: lo_key .. lo_key + n_vis - 1 (masked kernels:
+  // i - wl .. i + wr within 0 .. N-1; otherwise 0 .. N-1)
+  const int lo_key = CAUSAL ? myq - p.wl : 0;
+  const int hi_key = CAUSAL ? min(N - 1, myq + p.wr) : N - 1;
+  const uint32_t n_vis = hi_key >= lo_key ? (uint32_t)(hi_key - lo_key + 1) : 0u;
 
   // ---- Q^T as the B operand of S^T = K Q^T: column = row myq, k-slots = d
   bf16x8 qreg[kDK];
@@ -270,8 +275,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          bool vis = key < N && (!CAUSAL || (key <= myq + p.wr && key >= myq - p.wl));
-          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+          s[kb][r] = in_window(key, lo_key, n_vis) ? s[kb][r] : -INFINITY;
         }
     }
 
