@@ -155,3 +155,22 @@ def test_backward_empty_is_noop():
         dq, dk, dv = fa_backward(z, z, z, z, z, lse, causal=True)
         torch.cuda.synchronize()
         assert dq.numel() == 0
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_many_short_heads(d):
+    """B*H = 4096 heads of 17 rows (every K/V head count a multiple of 8, so the
+    launches hand heads to XCDs whole): sampled heads against the oracle."""
+    shape = (64, 64, 17, d)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = draw(shape, 48 + d, with_grad=True)
+    for causal in (True, False):
+        log(f"case many short heads {shape} causal={causal}")
+        outs = _fwd_bwd(q, k, v, do, scale, causal)
+        heads = sample_heads(shape[0], shape[1], 6, seed=d)
+        o = outs[0].float().cpu().numpy()
+        for b, h in heads:
+            ro, _ = oracle.forward_head(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), scale,
+                                        causal)
+            check_o(o[b, h], ro, f"{shape} b={b} h={h}")
+        _compare_heads(q, k, v, do, scale, causal, heads, outs, f"many heads d={d}")
