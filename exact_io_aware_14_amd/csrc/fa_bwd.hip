@@ -523,8 +523,13 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   if (myq < N) store_rows<D>(p.dq + (head + myq) * D, dqacc, p.scale, half);
 }
 
+// At d = 64 without a mask, four waves per SIMD (128 registers, two
+// workgroups per CU) beat two by 6-7% even though the dQ job then keeps a few
+// values in scratch; with a mask the extra scratch traffic of the masked
+// loops cancels the gain, so masked kernels keep two.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_grads_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 && !CAUSAL ? 4 : 1)
+void bwd_grads_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[GLayout<D>::kBytes];
   const Job job = job_of<CAUSAL>(p);
   if (job.is_dq)
