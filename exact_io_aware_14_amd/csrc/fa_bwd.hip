@@ -439,6 +439,27 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
     const unsigned char* kt = smem + LY::kKt + ST * LY::kTileBytes;
     const unsigned char* vt = smem + LY::kVt + ST * LY::kTileBytes;
 
+    // dQ^T += K^T dS^T for the 32 keys of half kb
+    auto accumulate = [&](int kb, const uint32_t* dsk_kb) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int rb = (kb * 32 + m * 16) * D * 2;
+        bf16x8 ka[kDB];
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+          ka[db] = lds_tr_pair(kt + rb + off.tr[db][0], kt + rb + off.tr[db][1]);
+        const uint4 du = {dsk_kb[4 * m], dsk_kb[4 * m + 1], dsk_kb[4 * m + 2], dsk_kb[4 * m + 3]};
+        const bf16x8 b = as_bf16x8(du);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) dqacc[db] = mfma32(ka[db], b, dqacc[db]);
+      }
+    };
+
+    // both halves' S, dP and dS, then both halves' dQ products (the MFMAs of
+    // the second half's S and dP run under the first half's arithmetic); at
+    // d = 64, which runs four waves per SIMD in 128 registers, each half's
+    // dS goes into dQ at once instead, which keeps 8 registers fewer live
+    // (the products are added in the same order either way)
     uint32_t dsk[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -469,24 +490,12 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) dsk[kb][j] = pack_bf16x2(dsv[2 * j], dsv[2 * j + 1]);
+      if constexpr (D == 64) accumulate(kb, dsk[kb]);
     }
-
-    // ---- dQ^T += K^T dS^T
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int rb = (kb * 32 + m * 16) * D * 2;
-        bf16x8 ka[kDB];
-#pragma unroll
-        for (int db = 0; db < kDB; ++db)
-          ka[db] = lds_tr_pair(kt + rb + off.tr[db][0], kt + rb + off.tr[db][1]);
-        const uint4 du = {dsk[kb][4 * m], dsk[kb][4 * m + 1], dsk[kb][4 * m + 2],
-                          dsk[kb][4 * m + 3]};
-        const bf16x8 b = as_bf16x8(du);
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) dqacc[db] = mfma32(ka[db], b, dqacc[db]);
-      }
+    if constexpr (D != 64) {
+      accumulate(0, dsk[0]);
+      accumulate(1, dsk[1]);
+    }
   };
 
   auto sync_fill = [&](int t) {
@@ -523,12 +532,11 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   if (myq < N) store_rows<D>(p.dq + (head + myq) * D, dqacc, p.scale, half);
 }
 
-// At d = 64 without a mask, four waves per SIMD (128 registers, two
-// workgroups per CU) beat two by 6-7% even though the dQ job then keeps a few
-// values in scratch; with a mask the extra scratch traffic of the masked
-// loops cancels the gain, so masked kernels keep two.
+// At d = 64 the kernels run four waves per SIMD (128 registers, two
+// workgroups per CU): 10-15% faster than two, the unmasked kernel without
+// spills, the masked one with 11 registers' worth in scratch.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 64 && !CAUSAL ? 4 : 1)
+__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1)
 void bwd_grads_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[GLayout<D>::kBytes];
   const Job job = job_of<CAUSAL>(p);
