@@ -64,7 +64,8 @@ GQA_WORKLOAD = "fwdbwd_causal_gqa_b4h32kv8n4096d128"
 WINDOW_WORKLOAD = "fwdbwd_window1024_b4h16n4096d128"
 METRIC = "attention TFLOP/s (fwd, fwd+bwd) bf16 on 1 MI355X; % of MFMA peak"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["exact_io_aware_14_amd/csrc/fa_common.h", "exact_io_aware_14_amd/csrc/fa_fwd.hip",
+KERNEL_SOURCES = ["exact_io_aware_14_amd/csrc/fa_common.h", "exact_io_aware_14_amd/csrc/fa_fwd_kernel.h",
+                  "exact_io_aware_14_amd/csrc/fa_fwd.hip", "exact_io_aware_14_amd/csrc/fa_fwd_w.hip",
                   "exact_io_aware_14_amd/csrc/fa_bwd_common.h", "exact_io_aware_14_amd/csrc/fa_bwd.hip",
                   "exact_io_aware_14_amd/csrc/fa_bwd_w.hip", "exact_io_aware_14_amd/csrc/fa_fp8.hip",
                   "exact_io_aware_14_amd/build.py"]

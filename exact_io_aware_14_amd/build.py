@@ -21,13 +21,15 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_w.hip", "fa_fp8.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_w.hip", "fa_bwd.hip", "fa_bwd_w.hip", "fa_fp8.hip"]
 
-# Per-source flags. The d = 256 backward kernels keep their accumulators in
-# place only under LLVM's "max-memory-clause" machine scheduler (with the
-# default one the register allocator rotates them through other registers
-# every tile); the other kernels are faster with the default.
-EXTRA_FLAGS = {"fa_bwd_w.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
+# Per-source flags, for the d = 256 kernels only (the others are as fast or
+# faster without them): the backward keeps its accumulators in place only
+# under LLVM's "max-memory-clause" machine scheduler (with the default one the
+# register allocator rotates them through other registers every tile), and
+# the forward runs faster with MFMA results in VGPRs where they fit.
+EXTRA_FLAGS = {"fa_bwd_w.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+               "fa_fwd_w.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
