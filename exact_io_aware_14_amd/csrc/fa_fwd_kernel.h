@@ -1,7 +1,7 @@
-// Forward exact attention for gfx950 (the kernel; fa_fwd.hip launches it
-// at d = 64 and 128, fa_fwd_w.hip at d = 256): one workgroup per (batch, head, block
-// of 128 query rows), four waves of 32 query rows each, two workgroups per
-// CU.
+// Forward exact attention for gfx950, the kernel (fa_fwd.hip launches it at
+// d = 64 and 128, fa_fwd_w.hip at d = 256): one workgroup per (batch, head,
+// block of 128 query rows), four waves of 32 query rows each, two
+// workgroups per CU at d = 128.
 //
 // Method: the tiled forward with a running row maximum m and row sum l, in
 // which the partial output of earlier key tiles is rescaled whenever m grows
