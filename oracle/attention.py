@@ -26,6 +26,16 @@ What it computes (per batch b and head h, all heads independent):
   the causal mask: every function's ``causal`` argument may also be a pair
   (left, right), key j visible to query i iff i - left <= j <= i + right, a
   bound of -1 meaning none on that side; True is (-1, 0), False (-1, -1).
+* Block-sparse attention is likewise named on the pages only as a coming
+  variant (nearauto.com page, section "今後の仕事": block-sparse attention)
+  and defined nowhere. The reading used: a mask over blocks of MASK_BLOCK
+  query rows x MASK_BLOCK keys of the score matrix; the scores of a block
+  the mask marks 0 are treated as masked keys (-inf), on top of the
+  causal or window mask. A row left with no visible key has O = 0 and
+  lse = -inf, and no gradient flows through it. Every function taking
+  ``causal`` also takes ``block_mask``: None (no mask), a 2-D array of
+  [ceil(N/MASK_BLOCK)] x [ceil(N/MASK_BLOCK)] entries (nonzero = computed),
+  or, for ``forward`` and ``backward``, one such array per (batch, head).
 * The per-row logsumexp lse_i = ln sum_j exp(scale * q_i . k_j) over visible
   keys is not on the pages; it is the row statistic the backward pass needs
   to recompute P without storing it (deepfa.ir page, section
@@ -58,6 +68,9 @@ import numpy as np
 # Rows of the score matrix formed at once; each output row depends only on its
 # own query row, so chunking rows changes nothing in the result.
 _ROW_CHUNK = 512
+
+# Query rows and keys per block of a block-sparse mask.
+MASK_BLOCK = 128
 
 
 def _check_head(q, k, v):
@@ -95,6 +108,25 @@ def _scores(q_rows, k, scale, row_ids, causal):
     return s
 
 
+def _apply_block_mask(s, row_ids, block_mask):
+    """Scores of the blocks a block-sparse mask marks 0 set to -inf."""
+    if block_mask is None:
+        return s
+    bm = np.asarray(block_mask) != 0
+    row_blocks = (np.asarray(row_ids) // MASK_BLOCK)[:, None]
+    key_blocks = (np.arange(s.shape[1]) // MASK_BLOCK)[None, :]
+    return np.where(bm[row_blocks, key_blocks], s, -np.inf)
+
+
+def _head_mask(block_mask, b, h):
+    """The block mask of head (b, h): None, one 2-D mask for every head, or
+    a [B, H, ...] stack of them."""
+    if block_mask is None:
+        return None
+    bm = np.asarray(block_mask)
+    return bm if bm.ndim == 2 else bm[b, h]
+
+
 def _row_softmax_stats(s):
     """Row max m and lse = m + ln sum exp(s - m) (decomposed softmax).
 
@@ -110,11 +142,12 @@ def _row_softmax_stats(s):
     return lse
 
 
-def forward_head(q, k, v, scale, causal, rows=None):
+def forward_head(q, k, v, scale, causal, rows=None, block_mask=None):
     """Exact attention output and logsumexp for one head.
 
     q, k, v: float64 [N, d]. rows: optional 1-D array of query indices to
-    compute (each row is independent of the others). Returns (O[rows], lse[rows]).
+    compute (each row is independent of the others). block_mask: see the
+    module docstring. Returns (O[rows], lse[rows]).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -127,7 +160,7 @@ def forward_head(q, k, v, scale, causal, rows=None):
     lse = np.zeros(rows.shape[0], dtype=np.float64)
     for start in range(0, rows.shape[0], _ROW_CHUNK):
         ids = rows[start:start + _ROW_CHUNK]
-        s = _scores(q[ids], k, scale, ids, causal)
+        s = _apply_block_mask(_scores(q[ids], k, scale, ids, causal), ids, block_mask)
         l_rows = _row_softmax_stats(s)
         with np.errstate(invalid="ignore"):
             p = np.exp(s - np.where(np.isfinite(l_rows), l_rows, 0.0)[:, None])
@@ -137,17 +170,20 @@ def forward_head(q, k, v, scale, causal, rows=None):
     return out, lse
 
 
-def probabilities_head(q, k, scale, causal):
-    """The full softmax matrix P (N x N) of one head; small N only."""
+def probabilities_head(q, k, scale, causal, block_mask=None):
+    """The full softmax matrix P (N x N) of one head; small N only. A row
+    with no visible key (possible under a block mask) is all zeros."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     ids = np.arange(q.shape[0])
-    s = _scores(q, k, scale, ids, causal)
+    s = _apply_block_mask(_scores(q, k, scale, ids, causal), ids, block_mask)
     lse = _row_softmax_stats(s)
-    return np.exp(s - lse[:, None])
+    with np.errstate(invalid="ignore"):
+        p = np.exp(s - lse[:, None])
+    return np.where(np.isfinite(lse)[:, None], p, 0.0)
 
 
-def backward_head(q, k, v, do, scale, causal):
+def backward_head(q, k, v, do, scale, causal, block_mask=None):
     """Gradients (dQ, dK, dV) of sum(dO * O) for one head, O = attention(q,k,v).
 
     Materialises the full N x N matrices. The forward output used for
@@ -158,7 +194,7 @@ def backward_head(q, k, v, do, scale, causal):
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     _check_head(q, k, v)
-    p = probabilities_head(q, k, scale, causal)
+    p = probabilities_head(q, k, scale, causal, block_mask)
     o = p @ v
     d_row = np.sum(do * o, axis=1)
     dp = do @ v.T
@@ -182,10 +218,11 @@ def kv_head(h, heads, kv_heads):
     return h // (heads // kv_heads)
 
 
-def forward(q, k, v, scale, causal):
+def forward(q, k, v, scale, causal, block_mask=None):
     """Batched forward: q [B, H, N, d], k and v [B, Hkv, N, d] float64 with
     Hkv dividing H (Hkv = H: multi-head) -> (O [B, H, N, d], lse [B, H, N]).
-    Query head h attends over K/V head kv_head(h, H, Hkv)."""
+    Query head h attends over K/V head kv_head(h, H, Hkv); block_mask is per
+    query head."""
     q = np.asarray(q, dtype=np.float64)
     bsz, heads, n, d = q.shape
     kv_heads = np.shape(k)[1]
@@ -194,11 +231,12 @@ def forward(q, k, v, scale, causal):
     for b in range(bsz):
         for h in range(heads):
             g = kv_head(h, heads, kv_heads)
-            out[b, h], lse[b, h] = forward_head(q[b, h], k[b, g], v[b, g], scale, causal)
+            out[b, h], lse[b, h] = forward_head(q[b, h], k[b, g], v[b, g], scale, causal,
+                                                block_mask=_head_mask(block_mask, b, h))
     return out, lse
 
 
-def backward(q, k, v, do, scale, causal):
+def backward(q, k, v, do, scale, causal, block_mask=None):
     """Batched backward over the shapes of ``forward`` -> (dQ, dK, dV). A K/V
     head read by several query heads receives the sum of their gradients (the
     chain rule for a shared input)."""
@@ -210,7 +248,8 @@ def backward(q, k, v, do, scale, causal):
     for b in range(q.shape[0]):
         for h in range(heads):
             g = kv_head(h, heads, kv_heads)
-            dq[b, h], dk_h, dv_h = backward_head(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+            dq[b, h], dk_h, dv_h = backward_head(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal,
+                                                 block_mask=_head_mask(block_mask, b, h))
             dk[b, g] += dk_h
             dv[b, g] += dv_h
     return dq, dk, dv

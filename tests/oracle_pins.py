@@ -425,6 +425,141 @@ def pin_window_brute_force():
             assert abs(lse[i] - math.log(tot)) < 1e-12
 
 
+# ---------------------------------------------------------------- block-sparse masks
+# A mask over blocks of 128 query rows x 128 keys (the reading stated in
+# oracle/attention.py); the pins expand it element by element themselves.
+
+BLOCK = 128
+
+
+def _expand_block_mask(bm, n):
+    keep = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        for j in range(n):
+            keep[i, j] = bm[i // BLOCK][j // BLOCK] != 0
+    return keep
+
+
+def _window_keep(n, left, right):
+    keep = np.ones((n, n), dtype=bool)
+    for i in range(n):
+        for j in range(n):
+            keep[i, j] = (left < 0 or j >= i - left) and (right < 0 or j <= i + right)
+    return keep
+
+
+def _random_block_mask(rng, nb, diagonal=True):
+    bm = (rng.random((nb, nb)) < 0.5).astype(np.uint8)
+    if diagonal:
+        np.fill_diagonal(bm, 1)
+    return bm
+
+
+def pin_block_mask_all_ones():
+    # an all-ones block mask is no block mask at all: the same arithmetic, bitwise
+    rng = np.random.default_rng(41)
+    n, d = 300, 6
+    q, k, v = _rand_head(rng, n, d)
+    do = rng.standard_normal((n, d))
+    for causal in (True, False, (40, 7)):
+        ones = np.ones((3, 3), dtype=np.uint8)
+        o1, l1 = A.forward_head(q, k, v, 0.4, causal)
+        o2, l2 = A.forward_head(q, k, v, 0.4, causal, block_mask=ones)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), f"all-ones mask {causal}"
+        for g1, g2 in zip(A.backward_head(q, k, v, do, 0.4, causal),
+                          A.backward_head(q, k, v, do, 0.4, causal, block_mask=ones)):
+            assert np.array_equal(g1, g2), f"all-ones mask gradients {causal}"
+
+
+def pin_block_mask_vs_torch():
+    rng = np.random.default_rng(42)
+    n, d, scale = 300, 8, 0.5
+    for causal, (left, right) in ((True, (-1, 0)), (False, (-1, -1)), ((60, 20), (60, 20))):
+        q, k, v = _rand_head(rng, n, d)
+        do = rng.standard_normal((n, d))
+        bm = _random_block_mask(rng, 3)  # the diagonal blocks keep every row non-empty
+        keep = torch.tensor(_expand_block_mask(bm, n) & _window_keep(n, left, right))
+        t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v)]
+        sc = (t[0] @ t[1].T * scale).masked_fill(~keep, -math.inf)
+        o_t = torch.softmax(sc, dim=-1) @ t[2]
+        (o_t * torch.tensor(do)).sum().backward()
+        o, lse = A.forward_head(q, k, v, scale, causal, block_mask=bm)
+        what = f"block mask {bm.tolist()} {causal}"
+        _close(o, o_t.detach().numpy(), 1e-12, f"O vs torch {what}")
+        _close(lse, torch.logsumexp(sc, dim=-1).detach().numpy(), 1e-12, f"lse vs torch {what}")
+        grads = A.backward_head(q, k, v, do, scale, causal, block_mask=bm)
+        for name, mine, ref in zip(("dQ", "dK", "dV"), grads, t):
+            _close(mine, ref.grad.numpy(), 1e-11, f"{name} vs autograd {what}")
+        # per-head masks through the batched calls
+        qb, kb, vb, dob = (np.stack([x, x[::-1].copy()])[None] for x in (q, k, v, do))
+        masks = np.stack([bm, bm.T])[None]
+        ob, lb = A.forward(qb, kb, vb, scale, causal, block_mask=masks)
+        _close(ob[0, 0], o, 1e-15, f"batched head 0 {what}")
+        o1, _ = A.forward_head(qb[0, 1], kb[0, 1], vb[0, 1], scale, causal, block_mask=bm.T)
+        _close(ob[0, 1], o1, 1e-15, f"batched head 1 {what}")
+
+
+def pin_block_mask_brute_force():
+    rng = np.random.default_rng(43)
+    n, d, scale = 260, 2, 0.8  # three blocks, the last one 4 rows
+    q, k, v = _rand_head(rng, n, d)
+    bm = _random_block_mask(rng, 3)
+    for causal in (True, False):
+        o, lse = A.forward_head(q, k, v, scale, causal, block_mask=bm)
+        for i in (0, 5, 127, 128, 200, 255, 256, 259):
+            keys = [j for j in range(n) if bm[i // BLOCK][j // BLOCK] and (not causal or j <= i)]
+            w = [math.exp(scale * sum(q[i, c] * k[j, c] for c in range(d))) for j in keys]
+            tot = sum(w)
+            for c in range(d):
+                ref = sum(wj * v[j, c] for wj, j in zip(w, keys)) / tot
+                assert abs(o[i, c] - ref) < 1e-12, f"brute force block mask row {i} {causal}"
+            assert abs(lse[i] - math.log(tot)) < 1e-12
+
+
+def pin_block_mask_empty_rows():
+    # query block 1 sees nothing: its O is 0, its lse -inf, its dQ 0; the
+    # other rows and every dK, dV are those of attention over the other rows
+    # alone (torch, which cannot take an empty row)
+    rng = np.random.default_rng(44)
+    n, d, scale = 300, 5, 0.6
+    q, k, v = _rand_head(rng, n, d)
+    do = rng.standard_normal((n, d))
+    bm = np.array([[1, 0, 1], [0, 0, 0], [0, 1, 1]], dtype=np.uint8)
+    o, lse = A.forward_head(q, k, v, scale, False, block_mask=bm)
+    empty = np.arange(128, 256)
+    live = np.concatenate([np.arange(128), np.arange(256, n)])
+    assert np.all(o[empty] == 0.0) and np.all(lse[empty] == -np.inf), "empty rows"
+    dq, dk, dv = A.backward_head(q, k, v, do, scale, False, block_mask=bm)
+    assert np.all(dq[empty] == 0.0), "no gradient through an empty row"
+    keep = torch.tensor(_expand_block_mask(bm, n)[live])
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q[live], k, v)]
+    sc = (t[0] @ t[1].T * scale).masked_fill(~keep, -math.inf)
+    o_t = torch.softmax(sc, dim=-1) @ t[2]
+    (o_t * torch.tensor(do[live])).sum().backward()
+    _close(o[live], o_t.detach().numpy(), 1e-12, "live rows O")
+    _close(dq[live], t[0].grad.numpy(), 1e-11, "live rows dQ")
+    _close(dk, t[1].grad.numpy(), 1e-11, "dK from the live rows")
+    _close(dv, t[2].grad.numpy(), 1e-11, "dV from the live rows")
+
+
+def pin_block_diagonal_segments():
+    # a block-diagonal mask is independent attention over each 128-row segment
+    rng = np.random.default_rng(45)
+    n, d, scale = 384, 4, 0.7
+    q, k, v = _rand_head(rng, n, d)
+    do = rng.standard_normal((n, d))
+    eye = np.eye(3, dtype=np.uint8)
+    o, lse = A.forward_head(q, k, v, scale, False, block_mask=eye)
+    grads = A.backward_head(q, k, v, do, scale, False, block_mask=eye)
+    for s in range(3):
+        seg = slice(s * BLOCK, (s + 1) * BLOCK)
+        os_, ls_ = A.forward_head(q[seg], k[seg], v[seg], scale, False)
+        _close(o[seg], os_, 1e-14, f"segment {s} O")
+        _close(lse[seg], ls_, 1e-14, f"segment {s} lse")
+        for g, gs in zip(grads, A.backward_head(q[seg], k[seg], v[seg], do[seg], scale, False)):
+            _close(g[seg], gs, 1e-13, f"segment {s} gradients")
+
+
 # ---------------------------------------------------------------- FP8 with incoherent processing
 
 def pin_fp8_e4m3_golden():
@@ -586,7 +721,9 @@ ALL_PINS = [pin_golden_forward, pin_golden_backward, pin_vs_torch_sdpa,
             pin_backward_vs_autograd, pin_finite_differences, pin_brute_force,
             pin_online_recurrence, pin_forward_invariants, pin_backward_invariants,
             pin_gqa_vs_autograd, pin_gqa_finite_differences, pin_window_special_cases,
-            pin_window_vs_torch, pin_window_brute_force, pin_fp8_e4m3_golden,
+            pin_window_vs_torch, pin_window_brute_force, pin_block_mask_all_ones,
+            pin_block_mask_vs_torch, pin_block_mask_brute_force, pin_block_mask_empty_rows,
+            pin_block_diagonal_segments, pin_fp8_e4m3_golden,
             pin_fp8_e4m3_grid, pin_fp8_scales, pin_fp8_v_blocks, pin_fp8_forward_golden,
             pin_fp8_pv_error_bound, pin_fp8_hadamard, pin_fp8_rotation_is_exact, pin_fp8_error_bound,
             pin_fp8_incoherence_lowers_error]

@@ -46,8 +46,8 @@ def _stats_max_only(s):
 
 
 def _bwd_variant(kind):
-    def bwd(q, k, v, do, scale, causal):
-        p = A.probabilities_head(q, k, scale, causal)
+    def bwd(q, k, v, do, scale, causal, block_mask=None):
+        p = A.probabilities_head(q, k, scale, causal, block_mask)
         o = p @ v
         d_row = np.sum(do * o, axis=1)
         dp = do @ v.T
@@ -67,11 +67,11 @@ def _bwd_variant(kind):
     return bwd
 
 
-def _fwd_transposed_p(q, k, v, scale, causal, rows=None):
-    p = A.probabilities_head(q, k, scale, causal)
+def _fwd_transposed_p(q, k, v, scale, causal, rows=None, block_mask=None):
+    p = A.probabilities_head(q, k, scale, causal, block_mask)
     o = p.T @ v
     ids = np.arange(q.shape[0]) if rows is None else rows
-    lse = A._ORIG["forward_head"](q, k, v, scale, causal, rows)[1]
+    lse = A._ORIG["forward_head"](q, k, v, scale, causal, rows, block_mask=block_mask)[1]
     return o[ids], lse
 
 
@@ -83,7 +83,7 @@ def _kv_head_reversed(h, heads, kv_heads):
     return (heads - 1 - h) // (heads // kv_heads)
 
 
-def _backward_not_summed(q, k, v, do, scale, causal):
+def _backward_not_summed(q, k, v, do, scale, causal, block_mask=None):
     heads, kv_heads = q.shape[1], k.shape[1]
     dq = np.zeros_like(q)
     dk = np.zeros(np.shape(k))
@@ -92,7 +92,8 @@ def _backward_not_summed(q, k, v, do, scale, causal):
         for h in range(heads):
             g = A.kv_head(h, heads, kv_heads)
             dq[b, h], dk[b, g], dv[b, g] = A.backward_head(q[b, h], k[b, g], v[b, g], do[b, h],
-                                                        scale, causal)
+                                                        scale, causal,
+                                                        block_mask=A._head_mask(block_mask, b, h))
     return dq, dk, dv
 
 
@@ -112,6 +113,28 @@ def _window_variant(kind):
             s = np.where(keys <= hi, s, -np.inf)
         return s
     return scores
+
+
+def _block_mask_variant(kind):
+    def apply(s, row_ids, block_mask):
+        if block_mask is None or kind == "ignored":
+            return s
+        size = 64 if kind == "size_64" else 128
+        bm = np.asarray(block_mask) != 0
+        rb = (np.asarray(row_ids) // size)[:, None]
+        kb = (np.arange(s.shape[1]) // size)[None, :]
+        if kind == "size_64":
+            rb, kb = np.minimum(rb, bm.shape[0] - 1), np.minimum(kb, bm.shape[1] - 1)
+        keep = bm[kb, rb] if kind == "transposed" else bm[rb, kb]
+        return np.where(keep, s, -np.inf)
+    return apply
+
+
+def _probabilities_empty_rows_kept(q, k, scale, causal, block_mask=None):
+    ids = np.arange(q.shape[0])
+    s = A._apply_block_mask(A._scores(q, k, scale, ids, causal), ids, block_mask)
+    lse = A._row_softmax_stats(s)
+    return np.exp(s - lse[:, None])
 
 
 def _e4m3_variant(kind):
@@ -225,6 +248,10 @@ MUTATIONS = {
     "window_left_bound_strict": ("_scores", _window_variant("left_strict")),
     "window_bounds_swapped": ("_scores", _window_variant("swapped")),
     "window_right_bound_one_wide": ("_scores", _window_variant("right_wide")),
+    "block_mask_transposed": ("_apply_block_mask", _block_mask_variant("transposed")),
+    "block_mask_blocks_of_64": ("_apply_block_mask", _block_mask_variant("size_64")),
+    "block_mask_ignored": ("_apply_block_mask", _block_mask_variant("ignored")),
+    "block_mask_empty_rows_not_zeroed": ("probabilities_head", _probabilities_empty_rows_kept),
 }
 FP8_MUTATIONS = {
     "e4m3_two_mantissa_bits": ("e4m3_round", _e4m3_variant("two_mantissa_bits")),
