@@ -33,9 +33,16 @@ A fifth, `d256`, times the forward+backward step at head dimension 256:
 B=4, H=8, N=4096, d=256, causal (seed 8), through the _gqa calls with
 H_kv = H.
 
+A sixth, `block_sparse`, times it on the causal workload B=4, H=16,
+N=4096, d=128 (seed 9) with a block-sparse mask per query head (each
+128 x 128 block below the diagonal kept with probability 1/2, the diagonal
+blocks always) through the _block_sparse calls; its FLOP count is 4*d per
+visible (query, key) pair, counted exactly from the mask.
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
                        [--copy-calibration] [--no-gqa] [--gqa-only] [--no-window]
                        [--window-only] [--no-fp8] [--fp8-only] [--no-d256] [--d256-only]
+                       [--no-block-sparse] [--block-sparse-only]
 --copy-calibration first runs a plain device copy of 1 GiB (torch's copy
 kernel), whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic
 counters of the attention kernels in the same profiled run.
@@ -62,6 +69,7 @@ D256_WORKLOAD = "fwdbwd_causal_b4h8n4096d256"
 WORKLOAD = "fwdbwd_causal_b4h16n4096d128"
 GQA_WORKLOAD = "fwdbwd_causal_gqa_b4h32kv8n4096d128"
 WINDOW_WORKLOAD = "fwdbwd_window1024_b4h16n4096d128"
+BLOCK_SPARSE_WORKLOAD = "fwdbwd_causal_blocksparse50_b4h16n4096d128"
 METRIC = "attention TFLOP/s (fwd, fwd+bwd) bf16 on 1 MI355X; % of MFMA peak"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["exact_io_aware_14_amd/csrc/fa_common.h", "exact_io_aware_14_amd/csrc/fa_fwd_kernel.h",
@@ -89,8 +97,29 @@ def visible_pairs(n, left, right):
     return total
 
 
+def block_sparse_pairs(w):
+    """Visible (query, key) pairs of all heads of a block-sparse workload:
+    per nonzero block of each head's mask, its pairs under the causal mask
+    (all of them without it)."""
+    import numpy as np
+
+    from exact_io_aware_14_amd.inputs import MASK_BLOCK, workload_block_mask
+
+    nb = (w.N + MASK_BLOCK - 1) // MASK_BLOCK
+    i = np.arange(w.N)
+    seen = (i[None, :] <= i[:, None]) if w.causal else np.ones((w.N, w.N), dtype=bool)
+    blk = i // MASK_BLOCK
+    per_block = np.zeros((nb, nb), dtype=np.int64)
+    np.add.at(per_block, (blk[:, None].repeat(w.N, 1)[seen], blk[None, :].repeat(w.N, 0)[seen]),
+              1)
+    mask = workload_block_mask(w).numpy() != 0
+    return int((mask * per_block).sum())
+
+
 def counted_flops(w):
-    if w.window_left >= 0 or w.window_right >= 0:
+    if w.block_density > 0:
+        fwd = 4.0 * w.d * block_sparse_pairs(w)
+    elif w.window_left >= 0 or w.window_right >= 0:
         fwd = 4.0 * w.B * w.H * w.d * visible_pairs(w.N, w.window_left, w.window_right)
     else:
         fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
@@ -161,11 +190,13 @@ def measure_variant(name, steps, warmup):
     import torch
 
     import exact_io_aware_14_amd as fa
-    from exact_io_aware_14_amd.inputs import by_name, draw
+    from exact_io_aware_14_amd.inputs import by_name, draw, workload_block_mask
 
     w = by_name(name)
     dev = torch.device("cuda:0")
     q, k, v, do = (x.to(dev) for x in draw(w.shape, w.seed, with_grad=True, kv_heads=w.kv_heads))
+    sparse = w.block_density > 0
+    bm = workload_block_mask(w).to(dev) if sparse else None
     o = torch.empty_like(q)
     lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -173,11 +204,14 @@ def measure_variant(name, steps, warmup):
     stream = torch.cuda.current_stream()
     window = w.window_left >= 0 or w.window_right >= 0
     win = (w.window_left, w.window_right)
+    causal_win = (-1, 0) if w.causal else (-1, -1)
 
     def step(ev):
         if ev is not None:
             ev[0].record(stream)
-        if window:
+        if sparse:
+            fa.fa_forward_block_sparse(q, k, v, bm, *causal_win, w.scale, o, lse, stream=stream)
+        elif window:
             fa.fa_forward_window(q, k, v, *win, w.scale, o, lse, stream=stream)
         else:
             fa.fa_forward_gqa(q, k, v, w.scale, w.causal, o, lse, stream=stream)
@@ -186,7 +220,10 @@ def measure_variant(name, steps, warmup):
         fa.fa_backward_prep(o, do, lse, ws, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        if window:
+        if sparse:
+            fa.fa_backward_grads_block_sparse(q, k, v, do, lse, ws, bm, *causal_win, w.scale, dq,
+                                              dk, dv, stream=stream)
+        elif window:
             fa.fa_backward_grads_window(q, k, v, do, lse, ws, *win, w.scale, dq, dk, dv,
                                         stream=stream)
         else:
@@ -202,6 +239,9 @@ def measure_variant(name, steps, warmup):
         out["window"] = [w.window_left, w.window_right]
     else:
         out["causal"] = w.causal
+    if sparse:
+        out["block_density"] = w.block_density
+        out["mask_blocks_kept"] = round(float(bm.float().mean()), 4)
     out.update({"steps": steps,
                 "fwdbwd_tflops": round((fwd_f + bwd_f) / (step_ms * 1e-3) / 1e12, 2),
                 "fwd_tflops": round(fwd_f / (fwd_ms * 1e-3) / 1e12, 2),
@@ -289,6 +329,9 @@ def main():
     ap.add_argument("--no-d256", action="store_true")
     ap.add_argument("--d256-only", action="store_true",
                     help="time only the head-dimension-256 step (for its profile)")
+    ap.add_argument("--no-block-sparse", action="store_true")
+    ap.add_argument("--block-sparse-only", action="store_true",
+                    help="time only the block-sparse step (for its profile)")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--fp8-only", action="store_true",
                     help="time only the FP8 forward (for its profile)")
@@ -314,6 +357,10 @@ def main():
     if args.window_only:
         print(json.dumps({"window": measure_variant(WINDOW_WORKLOAD, args.steps, args.warmup)}),
               flush=True)
+        return
+    if args.block_sparse_only:
+        print(json.dumps({"block_sparse": measure_variant(BLOCK_SPARSE_WORKLOAD, args.steps,
+                                                          args.warmup)}), flush=True)
         return
 
     import torch
@@ -413,6 +460,8 @@ def main():
         out["window"] = measure_variant(WINDOW_WORKLOAD, args.steps, args.warmup)
     if not args.no_d256:
         out["d256"] = measure_variant(D256_WORKLOAD, args.steps, args.warmup)
+    if not args.no_block_sparse:
+        out["block_sparse"] = measure_variant(BLOCK_SPARSE_WORKLOAD, args.steps, args.warmup)
     if not args.no_fp8:
         out["fp8"] = measure_fp8(args.steps, args.warmup)
     if not args.no_cpu_baseline:

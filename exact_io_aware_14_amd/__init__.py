@@ -16,11 +16,15 @@ import os
 __all__ = ["FAError", "fa_forward", "fa_forward_gqa", "fa_forward_window", "fa_forward_f32",
            "fa_backward", "fa_backward_gqa", "fa_backward_window", "fa_backward_prep",
            "fa_backward_grads", "fa_backward_grads_gqa", "fa_backward_grads_window",
+           "fa_forward_block_sparse", "fa_backward_block_sparse",
+           "fa_backward_grads_block_sparse", "MASK_BLOCK",
            "fa_backward_workspace_size", "fa_forward_fp8", "fa_fp8_prepare",
            "fa_forward_fp8_prepared", "fa_forward_fp8_workspace_size", "fa_strerror", "library",
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+MASK_BLOCK = 128  # query rows and keys per block of a block-sparse mask
 
 _lib = None
 
@@ -40,6 +44,7 @@ def library():
                 f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_14_amd.build`")
         lib = ctypes.CDLL(LIB_PATH)
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        ll = ctypes.c_longlong
         lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_forward.restype = i
         lib.fa_forward_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
@@ -57,7 +62,13 @@ def library():
                                               i, i, vp, sz, vp]),
                 ("fa_forward_fp8", [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]),
                 ("fa_fp8_prepare", [vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]),
-                ("fa_forward_fp8_prepared", [vp, sz, vp, vp, i, i, i, i, i, f, i, vp])):
+                ("fa_forward_fp8_prepared", [vp, sz, vp, vp, i, i, i, i, i, f, i, vp]),
+                ("fa_forward_block_sparse", [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, ll,
+                                             vp]),
+                ("fa_backward_block_sparse", [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
+                                              f, i, i, vp, ll, vp, sz, vp]),
+                ("fa_backward_grads_block_sparse", [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
+                                                    i, f, i, i, vp, ll, vp, sz, vp])):
             if hasattr(lib, name):  # an older build without them fails when they are called
                 getattr(lib, name).argtypes = argtypes
                 getattr(lib, name).restype = i
@@ -355,6 +366,109 @@ def fa_backward_grads_window(q, k, v, dout, lse, workspace, window_left, window_
                                                     workspace))
     if st != 0:
         raise FAError(st, "fa_backward_grads_window")
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------- block-sparse
+
+
+def _block_mask(mask, B, H, N, dev):
+    """The block mask as (tensor, head stride in bytes): uint8 or bool on the
+    device, [nb, nb] shared by all heads (stride 0) or [B, H, nb, nb] one per
+    query head, nb = ceil(N / 128), contiguous."""
+    torch = _torch()
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    if mask.dtype not in (torch.uint8, torch.bool):
+        raise TypeError(f"block_mask: expected uint8 or bool, got {mask.dtype}")
+    if tuple(mask.shape) == (nb, nb):
+        stride = 0
+    elif tuple(mask.shape) == (B, H, nb, nb):
+        stride = nb * nb
+    else:
+        raise ValueError(f"block_mask: expected shape {(nb, nb)} or {(B, H, nb, nb)}, "
+                         f"got {tuple(mask.shape)}")
+    if not mask.is_contiguous():
+        raise ValueError("block_mask must be contiguous")
+    if mask.device != dev:
+        raise ValueError(f"block_mask must be on {dev}")
+    return mask, stride
+
+
+def fa_forward_block_sparse(q, k, v, block_mask, window_left=-1, window_right=-1, scale=None,
+                            o=None, lse=None, stream=None):
+    """Block-sparse forward: blocks of 128 query rows x 128 keys whose mask
+    byte is 0 are masked, on top of the window (-1, -1: none; -1, 0:
+    causal); k, v may have fewer heads than q (see fa_forward_block_sparse
+    in fa.h)."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    Hkv = _kv_heads(q, k)
+    dev = q.device
+    _check(q, "q", torch.bfloat16, (B, H, N, d), dev)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, torch.bfloat16, (B, Hkv, N, d), dev)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(o, "o", torch.bfloat16, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    bm, stride = _block_mask(block_mask, B, H, N, dev)
+    scale = d ** -0.5 if scale is None else scale
+    st = library().fa_forward_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
+                                           Hkv, N, d, float(scale), int(window_left),
+                                           int(window_right), _ptr(bm), stride,
+                                           _stream(stream, q, k, v, o, lse, bm))
+    if st != 0:
+        raise FAError(st, "fa_forward_block_sparse")
+    return o, lse
+
+
+def fa_backward_block_sparse(q, k, v, o, dout, lse, block_mask, window_left=-1,
+                             window_right=-1, scale=None, dq=None, dk=None, dv=None,
+                             workspace=None, stream=None):
+    """Block-sparse backward, with the mask of the forward call (see
+    fa_backward_block_sparse in fa.h)."""
+    Hkv = _kv_heads(q, k)
+    shape, dev, (dq, dk, dv) = _bwd_check(
+        q, (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)), lse,
+        (("dq", dq), ("dk", dk), ("dv", dv)), Hkv)
+    ws, ws_bytes = _workspace(shape, dev, workspace)
+    B, H, N, d = shape
+    bm, stride = _block_mask(block_mask, B, H, N, dev)
+    scale = d ** -0.5 if scale is None else scale
+    st = library().fa_backward_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                            _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv,
+                                            N, d, float(scale), int(window_left),
+                                            int(window_right), _ptr(bm), stride, _ptr(ws),
+                                            ws_bytes,
+                                            _stream(stream, q, k, v, o, dout, lse, dq, dk, dv,
+                                                    ws, bm))
+    if st != 0:
+        raise FAError(st, "fa_backward_block_sparse")
+    return dq, dk, dv
+
+
+def fa_backward_grads_block_sparse(q, k, v, dout, lse, workspace, block_mask, window_left=-1,
+                                   window_right=-1, scale=None, dq=None, dk=None, dv=None,
+                                   stream=None):
+    """Second backward stage with a block-sparse mask (see fa.h)."""
+    Hkv = _kv_heads(q, k)
+    shape, dev, (dq, dk, dv) = _bwd_check(
+        q, (("q", q), ("k", k), ("v", v), ("dout", dout)), lse,
+        (("dq", dq), ("dk", dk), ("dv", dv)), Hkv)
+    if workspace is None or workspace.device != dev:
+        raise ValueError("workspace from fa_backward_prep is required, on the same device")
+    B, H, N, d = shape
+    bm, stride = _block_mask(block_mask, B, H, N, dev)
+    scale = d ** -0.5 if scale is None else scale
+    st = library().fa_backward_grads_block_sparse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, H,
+        Hkv, N, d, float(scale), int(window_left), int(window_right), _ptr(bm), stride,
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream, q, k, v, dout, lse, dq, dk, dv, workspace, bm))
+    if st != 0:
+        raise FAError(st, "fa_backward_grads_block_sparse")
     return dq, dk, dv
 
 

@@ -43,20 +43,31 @@ int check_ptrs(const void* const* ptrs, int n) {
   return FA_OK;
 }
 
+// The block mask of the block-sparse calls: any address (bytes), a
+// nonnegative head stride. nullptr stands for "no mask" inside the library,
+// so the block-sparse calls check it here.
+int check_mask(const uint8_t* mask, long long stride) {
+  if (mask == nullptr) return FA_ERR_NULL;
+  if (stride < 0) return FA_ERR_ARG;
+  return FA_OK;
+}
+
 bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d) {
   return ws != nullptr && aligned16(ws) && bytes >= fa_backward_workspace_size(B, H, N, d);
 }
 
 int forward_common(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int H, int Hkv, int N, int d, float scale, int wl, int wr, hipStream_t stream,
-                   bool f32) {
+                   bool f32, bool sparse = false, const uint8_t* mask = nullptr,
+                   long long mask_stride = 0) {
   bool empty = false;
   int st = check_common(B, H, Hkv, N, d, scale, wl, wr, &empty);
   if (st != FA_OK || empty) return st;
   const void* ptrs[5] = {q, k, v, o, lse};
   st = check_ptrs(ptrs, 5);
   if (st != FA_OK) return st;
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, wl, wr, stream, Hkv};
+  if (sparse && (st = check_mask(mask, mask_stride)) != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, wl, wr, stream, Hkv, mask, mask_stride};
   hipError_t e = f32 ? fa::launch_forward_f32(a) : fa::launch_forward_bf16(a);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -64,33 +75,37 @@ int forward_common(const void* q, const void* k, const void* v, void* o, float* 
 int grads_common(const void* q, const void* k, const void* v, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
                  int d, float scale, int wl, int wr, const void* workspace,
-                 size_t workspace_bytes, hipStream_t stream) {
+                 size_t workspace_bytes, hipStream_t stream, bool sparse = false,
+                 const uint8_t* mask = nullptr, long long mask_stride = 0) {
   bool empty = false;
   int st = check_common(B, H, Hkv, N, d, scale, wl, wr, &empty);
   if (st != FA_OK || empty) return st;
   const void* ptrs[8] = {q, k, v, dout, lse, dq, dk, dv};
   st = check_ptrs(ptrs, 8);
   if (st != FA_OK) return st;
+  if (sparse && (st = check_mask(mask, mask_stride)) != FA_OK) return st;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
   fa::BwdArgs a{q, k, v, nullptr, dout, lse, dq, dk, dv,
                 static_cast<float*>(const_cast<void*>(workspace)), B, H, N, d, scale, wl, wr,
-                stream, Hkv};
+                stream, Hkv, mask, mask_stride};
   return fa::launch_backward_grads(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int backward_common(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                     int H, int Hkv, int N, int d, float scale, int wl, int wr, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
+                    size_t workspace_bytes, hipStream_t stream, bool sparse = false,
+                    const uint8_t* mask = nullptr, long long mask_stride = 0) {
   bool empty = false;
   int st = check_common(B, H, Hkv, N, d, scale, wl, wr, &empty);
   if (st != FA_OK || empty) return st;
   const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
   st = check_ptrs(ptrs, 9);
   if (st != FA_OK) return st;
+  if (sparse && (st = check_mask(mask, mask_stride)) != FA_OK) return st;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace),
-                B, H, N, d, scale, wl, wr, stream, Hkv};
+                B, H, N, d, scale, wl, wr, stream, Hkv, mask, mask_stride};
   if (fa::launch_backward_prep(a) != hipSuccess) return FA_ERR_HIP;
   return fa::launch_backward_grads(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -250,6 +265,36 @@ int fa_backward_grads_window(const void* q, const void* k, const void* v, const 
                       window_right, workspace, workspace_bytes, stream);
 }
 
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int H_kv, int N, int d, float scale, int window_left,
+                            int window_right, const uint8_t* block_mask,
+                            long long block_mask_head_stride, hipStream_t stream) {
+  return forward_common(q, k, v, o, lse, B, H, H_kv, N, d, scale, window_left, window_right,
+                        stream, false, true, block_mask, block_mask_head_stride);
+}
+
+int fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             int B, int H, int H_kv, int N, int d, float scale, int window_left,
+                             int window_right, const uint8_t* block_mask,
+                             long long block_mask_head_stride, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale,
+                         window_left, window_right, workspace, workspace_bytes, stream, true,
+                         block_mask, block_mask_head_stride);
+}
+
+int fa_backward_grads_block_sparse(const void* q, const void* k, const void* v,
+                                   const void* dout, const float* lse, void* dq, void* dk,
+                                   void* dv, int B, int H, int H_kv, int N, int d, float scale,
+                                   int window_left, int window_right, const uint8_t* block_mask,
+                                   long long block_mask_head_stride, const void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  return grads_common(q, k, v, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, window_left,
+                      window_right, workspace, workspace_bytes, stream, true, block_mask,
+                      block_mask_head_stride);
+}
+
 size_t fa_forward_fp8_workspace_size(int B, int H, int H_kv, int N, int d) {
   bool empty = false;
   if (fp8_check(B, H, H_kv, N, d, 1.0f, -1, -1, &empty) != FA_OK || empty) return 0;
@@ -301,7 +346,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_ARG:
       return "invalid argument: causal must be 0 or 1, window bounds >= -1, scale finite, "
-             "signs +1 or -1";
+             "signs +1 or -1, block-mask head stride >= 0";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
     default: return "unknown status";

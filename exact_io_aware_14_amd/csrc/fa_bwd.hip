@@ -143,7 +143,7 @@ __device__ __forceinline__ void fill_tile(unsigned char* dst, const uint16_t* g,
 
 // ---------------------------------------------------------------- dK / dV
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
                                          unsigned char* smem) {
   using LY = GLayout<D>;
@@ -297,14 +297,56 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   // each step, the tile (and, the first time, the key block) is in LDS for
   // every wave, and every wave is done with the previous step, whose stage
   // the loads of the next step overwrite.
+  //
+  // Block-sparse kernels: query tile t of query head jq lies in query block
+  // t/2 of that head's mask, in column kblk. The walk still passes one
+  // barrier per tile but loads and computes only the tiles of nonzero
+  // blocks; the flag of the tile after next is loaded while the current one
+  // is computed, so its latency is hidden.
+  auto advance = [&](int& jq, int& t) {  // the tile after (jq, t); false at the end
+    if (t + 1 < ntiles) {
+      ++t;
+      return true;
+    }
+    if (jq + 1 < p.group) {
+      ++jq;
+      t = t0;
+      return true;
+    }
+    return false;
+  };
+  static_assert(!SPARSE || (kKeyBlock == kMaskBlock && 2 * kTile == kMaskBlock),
+                "a dK/dV job is one key block of the mask, two tiles one query block");
+  const size_t qhead_first = (size_t)bh * p.group;  // the group's first query head
+  auto flag = [&](int jq, int t) { return mask_byte(p, qhead_first + jq, t >> 1, kblk); };
+  uint32_t on_cur = 1, on_nxt = 1, on_after = 0;  // flags: this tile, the next, the one after
+  if constexpr (SPARSE) {
+    int j = 0, t = t0;
+    on_cur = t0 < ntiles ? __builtin_amdgcn_readfirstlane(flag(0, t0)) : 0u;
+    on_nxt = t0 < ntiles && advance(j, t) ? __builtin_amdgcn_readfirstlane(flag(j, t)) : 0u;
+  }
   int step = 0;
   auto sync_fill = [&](int jq, int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles)
-      fill(jq, t + 1, (step + 1) & 1);
-    else if (jq + 1 < p.group)
-      fill(jq + 1, t0, (step + 1) & 1);
+    if constexpr (SPARSE) {
+      int j1 = jq, t1 = t;
+      const bool has1 = advance(j1, t1);
+      int j2 = j1, t2 = t1;
+      on_after = has1 && advance(j2, t2) ? flag(j2, t2) : 0u;
+      if (has1 && on_nxt) fill(j1, t1, (step + 1) & 1);
+    } else {
+      if (t + 1 < ntiles)
+        fill(jq, t + 1, (step + 1) & 1);
+      else if (jq + 1 < p.group)
+        fill(jq + 1, t0, (step + 1) & 1);
+    }
+  };
+  auto rotate = [&]() {
+    if constexpr (SPARSE) {
+      on_cur = on_nxt;
+      on_nxt = __builtin_amdgcn_readfirstlane(on_after);
+    }
   };
   // Masked kernels: this wave's rows r0 .. r0+31 of tile t and its keys
   // kw0 .. kw0+31 all see each other for tiles tm1 .. tm2-1 (r0 >= kw0+31-wr
@@ -321,19 +363,22 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
     const int r0 = t * kTile + 32 * qh;
     return r0 + 31 >= kw0 - p.wr && r0 <= kw0 + 31 + p.wl;
   };
-  if (t0 < ntiles) fill(0, t0, 0);
+  if (t0 < ntiles && (!SPARSE || on_cur)) fill(0, t0, 0);
   for (int jq = 0; jq < p.group; ++jq) {
     for (int t = t0; t < tm1; ++t, ++step) {
       sync_fill(jq, t);
-      if (visible(t)) tile(t, step & 1, std::true_type());
+      if ((!SPARSE || on_cur) && visible(t)) tile(t, step & 1, std::true_type());
+      rotate();
     }
     for (int t = tm1; t < tm2; ++t, ++step) {
       sync_fill(jq, t);
-      tile(t, step & 1, std::false_type());
+      if (!SPARSE || on_cur) tile(t, step & 1, std::false_type());
+      rotate();
     }
     for (int t = tm2; t < ntiles; ++t, ++step) {
       sync_fill(jq, t);
-      if (visible(t)) tile(t, step & 1, std::true_type());
+      if ((!SPARSE || on_cur) && visible(t)) tile(t, step & 1, std::true_type());
+      rotate();
     }
   }
 
@@ -366,7 +411,7 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
 
 // ---------------------------------------------------------------- dQ
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
                                        unsigned char* smem) {
   using LY = GLayout<D>;
@@ -498,11 +543,43 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
     }
   };
 
+  // Block-sparse kernels: key tile t lies in key block t/2; waves 0-3 hold
+  // query block 2*qblk of the head's mask, waves 4-7 block 2*qblk+1. A tile
+  // is loaded if either block is nonzero and computed by the waves of a
+  // nonzero one; bit h of a flag is block 2*qblk+h. The bytes of the tile
+  // after next are loaded while the current one is computed.
+  static_assert(!SPARSE || (kQBlock == 2 * kMaskBlock && 2 * kTile == kMaskBlock),
+                "a dQ job is two query blocks of the mask, two tiles one key block");
+  const int qbm = 2 * qblk;
+  const uint32_t my_bit = 1u << (wave >> 2);
+  uint32_t on_cur = 3, on_nxt = 3, after0 = 0, after1 = 0;
+  auto both = [&](uint32_t b0, uint32_t b1) {
+    return (__builtin_amdgcn_readfirstlane(b0) != 0 ? 1u : 0u) |
+           (__builtin_amdgcn_readfirstlane(b1) != 0 ? 2u : 0u);
+  };
+  if constexpr (SPARSE) {
+    on_cur = kt0 < ntiles ? both(mask_byte(p, bh, qbm, kt0 >> 1), mask_byte(p, bh, qbm + 1, kt0 >> 1))
+                          : 0u;
+    on_nxt = kt0 + 1 < ntiles ? both(mask_byte(p, bh, qbm, (kt0 + 1) >> 1),
+                                     mask_byte(p, bh, qbm + 1, (kt0 + 1) >> 1))
+                              : 0u;
+  }
   auto sync_fill = [&](int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) fill(t + 1);
+    if constexpr (SPARSE) {
+      after0 = t + 2 < ntiles ? mask_byte(p, bh, qbm, (t + 2) >> 1) : 0u;
+      after1 = t + 2 < ntiles ? mask_byte(p, bh, qbm + 1, (t + 2) >> 1) : 0u;
+    }
+    if (t + 1 < ntiles && (!SPARSE || on_nxt)) fill(t + 1);
   };
+  auto rotate = [&]() {
+    if constexpr (SPARSE) {
+      on_cur = on_nxt;
+      on_nxt = both(after0, after1);
+    }
+  };
+  auto mine = [&]() { return !SPARSE || (on_cur & my_bit) != 0; };
   // Key tile t shows all of its keys to all of this wave's rows for tiles
   // tm1 .. tm2-1 (t*64 >= wave_last-wl and t*64+63 <= qw0+wr); the visible
   // tiles before and after cross a window edge (masked). Three loops (every
@@ -515,18 +592,21 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   }
   if (qw0 >= N) tm2 = tm1;  // no rows: every tile is skipped
   auto visible = [&](int t) { return t >= wt0 && t < wt1; };
-  fill(kt0);
+  if (!SPARSE || on_cur) fill(kt0);
   for (int t = kt0; t < tm1; ++t) {
     sync_fill(t);
-    if (visible(t)) tile(t, std::true_type());
+    if (mine() && visible(t)) tile(t, std::true_type());
+    rotate();
   }
   for (int t = tm1; t < tm2; ++t) {
     sync_fill(t);
-    tile(t, std::false_type());
+    if (mine()) tile(t, std::false_type());
+    rotate();
   }
   for (int t = tm2; t < ntiles; ++t) {
     sync_fill(t);
-    if (visible(t)) tile(t, std::true_type());
+    if (mine() && visible(t)) tile(t, std::true_type());
+    rotate();
   }
 
   if (myq < N) store_rows<D>(p.dq + (head + myq) * D, dqacc, p.scale, half);
@@ -535,15 +615,17 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
 // At d = 64 the kernels run four waves per SIMD (128 registers, two
 // workgroups per CU): 10-15% faster than two, the unmasked kernel without
 // spills, the masked one with 11 registers' worth in scratch.
-template <int D, bool CAUSAL>
+// SPARSE: a block-sparse mask on top of the window (CAUSAL kernels only).
+template <int D, bool CAUSAL, bool SPARSE = false>
 __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1)
 void bwd_grads_kernel(BwdParams p) {
+  static_assert(!SPARSE || CAUSAL, "block-sparse masks use the masked kernels");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[GLayout<D>::kBytes];
   const Job job = job_of<CAUSAL>(p);
   if (job.is_dq)
-    dq_job<D, CAUSAL>(p, job.bh, job.blk, smem);
+    dq_job<D, CAUSAL, SPARSE>(p, job.bh, job.blk, smem);
   else
-    dkdv_job<D, CAUSAL>(p, job.bh, job.blk, smem);
+    dkdv_job<D, CAUSAL, SPARSE>(p, job.bh, job.blk, smem);
 }
 
 template <int D>
@@ -557,11 +639,11 @@ hipError_t launch_prep_typed(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE = false>
 hipError_t launch_grads_typed(const BwdArgs& a) {
   const BwdParams p = make_params<D>(a);
   const dim3 grid((unsigned)((long long)(p.BH / p.group) * (p.nkb + p.group * p.nqb)));
-  hipLaunchKernelGGL((bwd_grads_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, a.stream, p);
+  hipLaunchKernelGGL((bwd_grads_kernel<D, CAUSAL, SPARSE>), grid, dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
 }
 
@@ -573,6 +655,11 @@ hipError_t launch_backward_prep(const BwdArgs& a) {
 }
 
 hipError_t launch_backward_grads(const BwdArgs& a) {
+  if (a.bmask != nullptr) {  // block-sparse: always the masked kernels
+    if (a.d == 64) return launch_grads_typed<64, true, true>(a);
+    if (a.d == 128) return launch_grads_typed<128, true, true>(a);
+    return launch_grads_wide_sparse(a);
+  }
   if (a.d == 64)
     return a.masked() ? launch_grads_typed<64, true>(a) : launch_grads_typed<64, false>(a);
   if (a.d == 256) return launch_grads_wide(a);

@@ -34,6 +34,12 @@ struct BwdParams {
   float scale;
   int wl, wr;       // masked kernels: key j visible to query i iff i-wl <= j <= i+wr
   int xcd_remap;
+  // block-sparse kernels: the mask of query head h (batch * query heads) at
+  // bmask + h * bm_stride, nbm x nbm bytes (query block, key block), a zero
+  // byte skipping the block
+  const uint8_t* bmask;
+  long long bm_stride;
+  int nbm;
 };
 
 // d = 256 job sizes
@@ -144,12 +150,23 @@ BwdParams make_params(const BwdArgs& a) {
   p.wl = a.wl < 0 ? kUnbounded : a.wl;
   p.wr = a.wr < 0 ? kUnbounded : a.wr;
   p.xcd_remap = (p.BH / p.group) % 8 == 0;
+  p.bmask = a.bmask;
+  p.bm_stride = a.bmask_stride;
+  p.nbm = (a.N + kMaskBlock - 1) / kMaskBlock;
   return p;
+}
+
+// Byte (qb, kb) of the block mask of query head h; 0 for a query block past
+// the last (the second half of a 256-row dQ job at the end of a head).
+__device__ __forceinline__ uint32_t mask_byte(const BwdParams& p, size_t h, int qb, int kb) {
+  if (qb >= p.nbm) return 0u;
+  return p.bmask[h * (size_t)p.bm_stride + (size_t)qb * p.nbm + kb];
 }
 
 }  // namespace
 
 // the grads launch at d = 256 (fa_bwd_w.hip)
 hipError_t launch_grads_wide(const BwdArgs& a);
+hipError_t launch_grads_wide_sparse(const BwdArgs& a);  // with a block-sparse mask
 
 }  // namespace fa

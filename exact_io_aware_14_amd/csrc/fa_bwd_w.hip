@@ -84,7 +84,7 @@ struct OffsetsW {
   }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __device__ __forceinline__ void dkdv_job_w(const BwdParams& p, int bh, int kblk,
                                            unsigned char* smem) {
   using LY = WLayout<D>;
@@ -228,14 +228,53 @@ __device__ __forceinline__ void dkdv_job_w(const BwdParams& p, int bh, int kblk,
     }
   };
 
+  // Block-sparse kernels: query tile t of query head jq lies in query block
+  // t/4 of that head's mask, in column kblk; only tiles of nonzero blocks
+  // are loaded and computed (the walk as at d = 128).
+  static_assert(!SPARSE || (kKeyBlockW == kMaskBlock && 4 * kQTileW == kMaskBlock),
+                "a dK/dV job is one key block of the mask, four tiles one query block");
+  auto advance = [&](int& jq, int& t) {  // the tile after (jq, t); false at the end
+    if (t + 1 < ntiles) {
+      ++t;
+      return true;
+    }
+    if (jq + 1 < p.group) {
+      ++jq;
+      t = t0;
+      return true;
+    }
+    return false;
+  };
+  const size_t qhead_first = (size_t)bh * p.group;  // the group's first query head
+  auto flag = [&](int jq, int t) { return mask_byte(p, qhead_first + jq, t >> 2, kblk); };
+  uint32_t on_cur = 1, on_nxt = 1, on_after = 0;  // flags: this tile, the next, the one after
+  if constexpr (SPARSE) {
+    int j = 0, t = t0;
+    on_cur = t0 < ntiles ? __builtin_amdgcn_readfirstlane(flag(0, t0)) : 0u;
+    on_nxt = t0 < ntiles && advance(j, t) ? __builtin_amdgcn_readfirstlane(flag(j, t)) : 0u;
+  }
   int step = 0;
   auto sync_fill = [&](int jq, int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles)
-      fill(jq, t + 1, (step + 1) & 1);
-    else if (jq + 1 < p.group)
-      fill(jq + 1, t0, (step + 1) & 1);
+    if constexpr (SPARSE) {
+      int j1 = jq, t1 = t;
+      const bool has1 = advance(j1, t1);
+      int j2 = j1, t2 = t1;
+      on_after = has1 && advance(j2, t2) ? flag(j2, t2) : 0u;
+      if (has1 && on_nxt) fill(j1, t1, (step + 1) & 1);
+    } else {
+      if (t + 1 < ntiles)
+        fill(jq, t + 1, (step + 1) & 1);
+      else if (jq + 1 < p.group)
+        fill(jq + 1, t0, (step + 1) & 1);
+    }
+  };
+  auto rotate = [&]() {
+    if constexpr (SPARSE) {
+      on_cur = on_nxt;
+      on_nxt = __builtin_amdgcn_readfirstlane(on_after);
+    }
   };
   // this wave's keys kw0 .. kw0+31 and the rows r0 .. r0+31 of tile t all
   // see each other for tiles tm1 .. tm2-1; the visible tiles before and
@@ -249,19 +288,22 @@ __device__ __forceinline__ void dkdv_job_w(const BwdParams& p, int bh, int kblk,
     const int r0 = t * kQTileW;
     return r0 + 31 >= kw0 - p.wr && r0 <= kw0 + 31 + p.wl;
   };
-  if (t0 < ntiles) fill(0, t0, 0);
+  if (t0 < ntiles && (!SPARSE || on_cur)) fill(0, t0, 0);
   for (int jq = 0; jq < p.group; ++jq) {
     for (int t = t0; t < tm1; ++t, ++step) {
       sync_fill(jq, t);
-      if (visible(t)) tile(t, step & 1, std::true_type());
+      if ((!SPARSE || on_cur) && visible(t)) tile(t, step & 1, std::true_type());
+      rotate();
     }
     for (int t = tm1; t < tm2; ++t, ++step) {
       sync_fill(jq, t);
-      tile(t, step & 1, std::false_type());
+      if (!SPARSE || on_cur) tile(t, step & 1, std::false_type());
+      rotate();
     }
     for (int t = tm2; t < ntiles; ++t, ++step) {
       sync_fill(jq, t);
-      if (visible(t)) tile(t, step & 1, std::true_type());
+      if ((!SPARSE || on_cur) && visible(t)) tile(t, step & 1, std::true_type());
+      rotate();
     }
   }
   if (mykey < N) {
@@ -270,7 +312,7 @@ __device__ __forceinline__ void dkdv_job_w(const BwdParams& p, int bh, int kblk,
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __device__ __forceinline__ void dq_job_w(const BwdParams& p, int bh, int qblk,
                                          unsigned char* smem) {
   using LY = WLayout<D>;
@@ -398,10 +440,30 @@ __device__ __forceinline__ void dq_job_w(const BwdParams& p, int bh, int qblk,
       }
   };
 
+  // Block-sparse kernels: the job is query block qblk of the head's mask;
+  // key tile t lies in key block t/2. Only tiles of nonzero blocks are
+  // loaded and computed; the flag of the tile after next is loaded while
+  // the current one is computed.
+  static_assert(!SPARSE || (kQBlockW == kMaskBlock && 2 * kKTileW == kMaskBlock),
+                "a dQ job is one query block of the mask, two tiles one key block");
+  uint32_t on_cur = 1, on_nxt = 1, on_after = 0;
+  if constexpr (SPARSE) {
+    on_cur = kt0 < ntiles ? __builtin_amdgcn_readfirstlane(mask_byte(p, bh, qblk, kt0 >> 1)) : 0u;
+    on_nxt = kt0 + 1 < ntiles
+                 ? __builtin_amdgcn_readfirstlane(mask_byte(p, bh, qblk, (kt0 + 1) >> 1))
+                 : 0u;
+  }
   auto sync_fill = [&](int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) fill(t + 1);
+    if constexpr (SPARSE) on_after = t + 2 < ntiles ? mask_byte(p, bh, qblk, (t + 2) >> 1) : 0u;
+    if (t + 1 < ntiles && (!SPARSE || on_nxt)) fill(t + 1);
+  };
+  auto rotate = [&]() {
+    if constexpr (SPARSE) {
+      on_cur = on_nxt;
+      on_nxt = __builtin_amdgcn_readfirstlane(on_after);
+    }
   };
   int tm1 = kt0, tm2 = wt1;
   if (CAUSAL) {
@@ -410,38 +472,44 @@ __device__ __forceinline__ void dq_job_w(const BwdParams& p, int bh, int qblk,
   }
   if (qw0 >= N) tm2 = tm1;
   auto visible = [&](int t) { return t >= wt0 && t < wt1; };
-  fill(kt0);
+  if (!SPARSE || on_cur) fill(kt0);
   for (int t = kt0; t < tm1; ++t) {
     sync_fill(t);
-    if (visible(t)) tile(t, std::true_type());
+    if ((!SPARSE || on_cur) && visible(t)) tile(t, std::true_type());
+    rotate();
   }
   for (int t = tm1; t < tm2; ++t) {
     sync_fill(t);
-    tile(t, std::false_type());
+    if (!SPARSE || on_cur) tile(t, std::false_type());
+    rotate();
   }
   for (int t = tm2; t < ntiles; ++t) {
     sync_fill(t);
-    if (visible(t)) tile(t, std::true_type());
+    if ((!SPARSE || on_cur) && visible(t)) tile(t, std::true_type());
+    rotate();
   }
 
   if (myq < N) store_rows<D>(p.dq + (head + myq) * D, dqacc, p.scale, half);
 }
 
-template <int D, bool CAUSAL>
+// SPARSE: a block-sparse mask on top of the window (CAUSAL kernels only).
+template <int D, bool CAUSAL, bool SPARSE = false>
 __global__ __launch_bounds__(kThreadsW, 1) void bwd_grads_kernel_w(BwdParams p) {
+  static_assert(!SPARSE || CAUSAL, "block-sparse masks use the masked kernels");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[WLayout<D>::kBytes];
   const Job job = job_of<CAUSAL>(p);
   if (job.is_dq)
-    dq_job_w<D, CAUSAL>(p, job.bh, job.blk, smem);
+    dq_job_w<D, CAUSAL, SPARSE>(p, job.bh, job.blk, smem);
   else
-    dkdv_job_w<D, CAUSAL>(p, job.bh, job.blk, smem);
+    dkdv_job_w<D, CAUSAL, SPARSE>(p, job.bh, job.blk, smem);
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool SPARSE = false>
 hipError_t launch_grads_w(const BwdArgs& a) {
   const BwdParams p = make_params<256>(a);
   const dim3 grid((unsigned)((long long)(p.BH / p.group) * (p.nkb + p.group * p.nqb)));
-  hipLaunchKernelGGL((bwd_grads_kernel_w<256, CAUSAL>), grid, dim3(kThreadsW), 0, a.stream, p);
+  hipLaunchKernelGGL((bwd_grads_kernel_w<256, CAUSAL, SPARSE>), grid, dim3(kThreadsW), 0,
+                     a.stream, p);
   return hipGetLastError();
 }
 
@@ -450,5 +518,7 @@ hipError_t launch_grads_w(const BwdArgs& a) {
 hipError_t launch_grads_wide(const BwdArgs& a) {
   return a.masked() ? launch_grads_w<true>(a) : launch_grads_w<false>(a);
 }
+
+hipError_t launch_grads_wide_sparse(const BwdArgs& a) { return launch_grads_w<true, true>(a); }
 
 }  // namespace fa

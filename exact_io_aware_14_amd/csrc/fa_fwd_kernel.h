@@ -64,6 +64,11 @@ struct FwdParams {
   int negate_q;  // scale < 0: Q is negated on load and |scale| is used
   int xcd_remap; // K/V heads grouped per XCD (requires BH / group % 8 == 0)
   int wl, wr;    // masked kernels: key j visible to query i iff i-wl <= j <= i+wr
+  // block-sparse kernels: the mask of query head bh at bmask + bh * bm_stride,
+  // nbm x nbm bytes (query block, key block), a zero byte skipping the block
+  const uint8_t* bmask;
+  long long bm_stride;
+  int nbm;
 };
 
 // Workgroup shape: four waves (128 query rows), two workgroups per CU at
@@ -83,9 +88,12 @@ struct Layout {
   static_assert(kFill >= 1 && kTileBytes % (1024 * kWaves) == 0, "tile must split over waves");
 };
 
-template <int D, int BC, bool CAUSAL, typename TIn, typename TOut>
+// SPARSE: a block-sparse mask on top of the window (CAUSAL kernels only).
+template <int D, int BC, bool CAUSAL, typename TIn, typename TOut, bool SPARSE = false>
 __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (D == 64 && sizeof(TIn) == 2 ? 4 : 2))
 void fwd_kernel(FwdParams p) {
+  static_assert(!SPARSE || (CAUSAL && kBR == kMaskBlock && 2 * BC == kMaskBlock),
+                "a workgroup is one query block of the mask, two tiles one key block");
   using LY = Layout<D, BC>;
   // stages 0 and 1 of the K and V tiles (row-major, swizzle rsw)
   __shared__ __attribute__((aligned(1024))) unsigned char k0[LY::kTileBytes];
@@ -329,6 +337,20 @@ void fwd_kernel(FwdParams p) {
     l_run += ls0 + ls1;
   };
 
+  // ---- block-sparse kernels: tile t lies in key block t/2 of the mask row
+  // of this query block; the workgroup still walks every tile (one barrier
+  // each) but loads and computes only those of nonzero blocks. The flag of
+  // tile t+2 is loaded while tile t is computed, so its latency is hidden.
+  const uint8_t* bm_row = nullptr;
+  uint32_t on_cur = 1, on_nxt = 1;  // flags of the current and the next tile
+  if constexpr (SPARSE) {
+    bm_row = p.bmask + (size_t)bh * (size_t)p.bm_stride + (size_t)qb * p.nbm;
+    on_cur = __builtin_amdgcn_readfirstlane((uint32_t)bm_row[t_first >> 1]);
+    on_nxt = t_first + 1 < t_end
+                 ? __builtin_amdgcn_readfirstlane((uint32_t)bm_row[(t_first + 1) >> 1])
+                 : 0u;
+  }
+
   // ---- tiles. K and V of tile t+1 load while tile t is computed: one
   // barrier per tile, after which tile t is in LDS for every wave and every
   // wave is done with tile t-1, whose stage the loads of tile t+1 overwrite.
@@ -337,18 +359,28 @@ void fwd_kernel(FwdParams p) {
                   unsigned char* vn) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < t_end) {
+    uint32_t on_after = 0;  // SPARSE: flag of tile t+2, loaded before the tile loads
+    if constexpr (SPARSE) {
+      if (t + 2 < t_end) on_after = bm_row[(t + 2) >> 1];
+    }
+    if (t + 1 < t_end && (!SPARSE || on_nxt)) {
       fill_tile(kg, t + 1, kn, fk);
       fill_tile(vg, t + 1, vn, fk);
     }
-    if (t >= wt_first && t < wt_end) {
+    if ((!SPARSE || on_cur) && t >= wt_first && t < wt_end) {
       qk(kc);
       softmax(t);
       pv(vc);
     }
+    if constexpr (SPARSE) {
+      on_cur = on_nxt;
+      on_nxt = __builtin_amdgcn_readfirstlane(on_after);
+    }
   };
-  fill_tile(kg, t_first, k0, fk);
-  fill_tile(vg, t_first, v0, fk);
+  if (!SPARSE || on_cur) {
+    fill_tile(kg, t_first, k0, fk);
+    fill_tile(vg, t_first, v0, fk);
+  }
   for (int t = t_first; t < t_end; t += 2) {
     step(t, k0, v0, k1, v1);
     if (t + 1 < t_end) step(t + 1, k1, v1, k0, v0);
@@ -382,7 +414,7 @@ void fwd_kernel(FwdParams p) {
 
 constexpr int kBC = 64;  // keys per tile
 
-template <int D, bool CAUSAL, typename TIn, typename TOut>
+template <int D, bool CAUSAL, typename TIn, typename TOut, bool SPARSE = false>
 hipError_t launch_typed(const FwdArgs& a) {
   FwdParams p;
   p.q = a.q;
@@ -402,8 +434,11 @@ hipError_t launch_typed(const FwdArgs& a) {
   p.wr = a.wr < 0 ? kUnbounded : a.wr;
   p.negate_q = a.scale < 0.0f;
   p.xcd_remap = (p.BH / p.group) % 8 == 0;
+  p.bmask = a.bmask;
+  p.bm_stride = a.bmask_stride;
+  p.nbm = (a.N + kMaskBlock - 1) / kMaskBlock;
   dim3 grid((unsigned)((long long)p.BH * p.nqb));
-  hipLaunchKernelGGL((fwd_kernel<D, kBC, CAUSAL, TIn, TOut>), grid,
+  hipLaunchKernelGGL((fwd_kernel<D, kBC, CAUSAL, TIn, TOut, SPARSE>), grid,
                      dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
 }
@@ -413,5 +448,6 @@ hipError_t launch_typed(const FwdArgs& a) {
 // the d = 256 launches (fa_fwd_w.hip)
 hipError_t launch_forward_wide_bf16(const FwdArgs& a);
 hipError_t launch_forward_wide_f32(const FwdArgs& a);
+hipError_t launch_forward_wide_sparse(const FwdArgs& a);  // block-sparse, bf16
 
 }  // namespace fa

@@ -16,6 +16,10 @@ hipError_t launch_forward_wide_bf16(const FwdArgs& a) {
                     : launch_typed<256, false, uint16_t, uint16_t>(a);
 }
 
+hipError_t launch_forward_wide_sparse(const FwdArgs& a) {
+  return launch_typed<256, true, uint16_t, uint16_t, true>(a);
+}
+
 hipError_t launch_forward_wide_f32(const FwdArgs& a) {
   return a.masked() ? launch_typed<256, true, float, float>(a)
                     : launch_typed<256, false, float, float>(a);

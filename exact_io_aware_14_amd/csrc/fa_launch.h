@@ -19,6 +19,11 @@ struct FwdArgs {
   int wl, wr;  // key j visible to query i iff i-wl <= j <= i+wr; -1: no bound on that side
   hipStream_t stream;
   int Hkv;  // K/V heads; divides H (H: multi-head attention)
+  // block-sparse mask (nullptr: none): per query head (b, h), at
+  // bmask + (b*H + h) * bmask_stride, ceil(N/kMaskBlock)^2 bytes, row-major
+  // (query block, key block); a zero byte skips that block
+  const uint8_t* bmask = nullptr;
+  long long bmask_stride = 0;
   bool masked() const { return wl >= 0 || wr >= 0; }
 };
 
@@ -38,12 +43,18 @@ struct BwdArgs {
   int wl, wr;  // key j visible to query i iff i-wl <= j <= i+wr; -1: no bound on that side
   hipStream_t stream;
   int Hkv;  // K/V heads of k, v, dk, dv; divides H (H: multi-head attention)
+  // block-sparse mask, as in FwdArgs
+  const uint8_t* bmask = nullptr;
+  long long bmask_stride = 0;
   bool masked() const { return wl >= 0 || wr >= 0; }
 };
 
 // A window bound that never cuts: larger than any distance between a query
 // and a key, small enough that i + kUnbounded and i - kUnbounded stay in int.
 constexpr int kUnbounded = 1 << 30;
+
+// Query rows and keys per block of a block-sparse mask.
+constexpr int kMaskBlock = 128;
 
 // FP8 forward: byte offsets of the workspace regions (each 256-byte
 // aligned) and its total size.

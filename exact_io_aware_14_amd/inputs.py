@@ -34,6 +34,8 @@ class Workload:
     Hkv: int = 0        # K/V heads shared by groups of query heads; 0: H (multi-head)
     window_left: int = -1   # local window (key j visible to query i iff
     window_right: int = -1  # i-left <= j <= i+right); -1: no bound on that side
+    block_density: float = 0.0  # block-sparse: a seeded mask per query head
+                                # (draw_block_mask); 0: no block mask
 
     @property
     def shape(self):
@@ -78,8 +80,17 @@ D256_WORKLOADS = [
 ]
 
 
+# Block-sparse attention: under the causal mask, each query head keeps each
+# 128 x 128 block below the diagonal with probability 1/2 and every diagonal
+# block (so no row is empty).
+BLOCK_SPARSE_WORKLOADS = [
+    Workload("fwdbwd_causal_blocksparse50_b4h16n4096d128", 4, 16, 4096, 128, True, True, "bf16",
+             9, block_density=0.5),
+]
+
+
 def by_name(name: str) -> Workload:
-    for w in WORKLOADS + GQA_WORKLOADS + WINDOW_WORKLOADS + D256_WORKLOADS:
+    for w in WORKLOADS + GQA_WORKLOADS + WINDOW_WORKLOADS + D256_WORKLOADS + BLOCK_SPARSE_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)
@@ -112,6 +123,52 @@ def draw_signs(d, seed):
     g = torch.Generator(device="cpu").manual_seed(int(seed))
     bits = torch.randint(0, 2, (d,), generator=g, dtype=torch.int8)
     return (1 - 2 * bits).to(torch.int8)
+
+
+MASK_BLOCK = 128  # query rows and keys per block of a block-sparse mask
+
+
+def draw_block_mask(N, seed, density=0.5, heads=(), diagonal=True, empty_rows=0):
+    """A seeded block-sparse mask: uint8 CPU tensor [*heads, nb, nb],
+    nb = ceil(N / 128), each byte 1 with probability ``density``.
+
+    diagonal: the diagonal blocks are set to 1 (no row is left without keys
+    under a causal mask). empty_rows: that many block rows, drawn at random
+    per head, are then set to 0 entirely (rows that see no key).
+    """
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    shape = tuple(heads) + (nb, nb)
+    bm = (torch.rand(shape, generator=g) < density).to(torch.uint8)
+    if diagonal:
+        bm[..., torch.arange(nb), torch.arange(nb)] = 1
+    if empty_rows:
+        flat = bm.reshape(-1, nb, nb)
+        for m in flat:
+            rows = torch.randperm(nb, generator=g)[:empty_rows]
+            m[rows, :] = 0
+    return bm
+
+
+def draw_segments(N, seed, heads=()):
+    """A block-diagonal mask [*heads, nb, nb] of seeded segments: consecutive
+    runs of 1 to 4 blocks see each other and nothing else (packed sequences
+    at block granularity)."""
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    bm = torch.zeros(tuple(heads) + (nb, nb), dtype=torch.uint8)
+    for m in bm.reshape(-1, nb, nb):
+        i = 0
+        while i < nb:
+            n = int(torch.randint(1, 5, (1,), generator=g))
+            m[i:i + n, i:i + n] = 1
+            i += n
+    return bm
+
+
+def workload_block_mask(w: Workload):
+    """The per-query-head block mask [B, H, nb, nb] of a block-sparse workload."""
+    return draw_block_mask(w.N, 1000 + w.seed, w.block_density, heads=(w.B, w.H))
 
 
 def draw_workload(w: Workload):

@@ -50,6 +50,7 @@
 #define FA_H
 
 #include <stddef.h>
+#include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -63,7 +64,7 @@ typedef enum {
     FA_ERR_HEADDIM = 3,   /* d not in {64, 128, 256} ({64, 128} for the FP8 calls) */
     FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
     FA_ERR_ARG = 5,       /* causal not 0/1, a window bound below -1, scale not finite,
-                             or an FP8 sign not +1/-1 */
+                             an FP8 sign not +1/-1, or a negative block-mask head stride */
     FA_ERR_WORKSPACE = 6, /* workspace missing, misaligned or too small */
     FA_ERR_HIP = 7        /* the HIP runtime reported an error at launch */
 } fa_status;
@@ -214,6 +215,51 @@ int fa_backward_grads_window(const void* q, const void* k, const void* v, const 
                              int B, int H, int H_kv, int N, int d, float scale, int window_left,
                              int window_right, const void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * Block-sparse attention. The nearauto.com FlashAttention-2 article names
+ * block-sparse attention only as coming work (section "今後の仕事"); the
+ * library reads it as a mask over blocks of 128 query rows x 128 keys:
+ *   block_mask : DEVICE bytes, for query head (b, h) at
+ *                block_mask + (b*H + h) * block_mask_head_stride, an
+ *                nb x nb row-major array, nb = ceil(N / 128): byte (I, J)
+ *                covers query rows 128I .. 128I+127 and keys 128J ..
+ *                128J+127. Zero: every key of block J is masked for every
+ *                row of block I; nonzero: the block is computed under the
+ *                window mask of window_left, window_right (as the _window
+ *                calls; -1, -1 for none, -1, 0 for causal).
+ *   block_mask_head_stride : bytes between the masks of consecutive query
+ *                heads, >= 0; 0 shares one mask among all heads. The caller
+ *                keeps (B*H - 1) * stride + nb*nb bytes readable. Grouped
+ *                K/V heads (H_kv < H) keep a mask per query head.
+ * A row that sees no key at all (its blocks all zero, or its window keys
+ * all in zero blocks) gets O = 0 and lse = -inf, and contributes nothing to
+ * dq, dk, dv; its own dq row is 0. Zero blocks are neither loaded nor
+ * computed: the work follows the number of nonzero blocks.
+ * Inputs are bf16 as in fa_forward_window / fa_backward_window, whose
+ * argument rules, workspace and results these calls share; a NULL
+ * block_mask returns FA_ERR_NULL (checked after the tensor pointers), a
+ * negative stride FA_ERR_ARG. The mask takes no alignment. The backward
+ * calls take the lse of the forward call with the same mask.
+ */
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int H_kv, int N, int d, float scale, int window_left,
+                            int window_right, const uint8_t* block_mask,
+                            long long block_mask_head_stride, hipStream_t stream);
+
+int fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             int B, int H, int H_kv, int N, int d, float scale, int window_left,
+                             int window_right, const uint8_t* block_mask,
+                             long long block_mask_head_stride, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+int fa_backward_grads_block_sparse(const void* q, const void* k, const void* v,
+                                   const void* dout, const float* lse, void* dq, void* dk,
+                                   void* dv, int B, int H, int H_kv, int N, int d, float scale,
+                                   int window_left, int window_right, const uint8_t* block_mask,
+                                   long long block_mask_head_stride, const void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * FP8 forward with incoherent processing. The pages describe FlashAttention-3

@@ -42,7 +42,8 @@ def test_every_declared_symbol_is_exported(lib):
             "fa_forward_gqa", "fa_backward_gqa", "fa_backward_grads_gqa",
             "fa_forward_window", "fa_backward_window", "fa_backward_grads_window",
             "fa_forward_fp8", "fa_fp8_prepare", "fa_forward_fp8_prepared",
-            "fa_forward_fp8_workspace_size"} <= set(names)
+            "fa_forward_fp8_workspace_size", "fa_forward_block_sparse",
+            "fa_backward_block_sparse", "fa_backward_grads_block_sparse"} <= set(names)
     raw = ctypes.CDLL(fa.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), f"{name} declared in include/ but not exported"
@@ -227,6 +228,46 @@ def test_window_validation(lib):
     assert grads_w(wb=ws - 4) == FA_ERR_WORKSPACE
 
 
+def test_block_sparse_validation(lib):
+    """The block-sparse calls check as the _window calls, then the mask: NULL is
+    FA_ERR_NULL (after the tensor pointers), a negative head stride FA_ERR_ARG;
+    the mask takes any address."""
+    ws = 2 * 4 * 16 * 4
+
+    def fwd_s(wl=-1, wr=0, H=4, Hkv=2, ptrs=None, N=16, d=64, m=P, ms=0):
+        ptrs = ptrs or [P] * 5
+        return lib.fa_forward_block_sparse(*ptrs, 1, H, Hkv, N, d, 0.125, wl, wr, m, ms, NULL)
+
+    def bwd_s(wl=-1, wr=0, H=4, Hkv=2, ptrs=None, N=16, d=64, m=P, ms=0, wb=ws):
+        ptrs = ptrs or [P] * 9
+        return lib.fa_backward_block_sparse(*ptrs, 1, H, Hkv, N, d, 0.125, wl, wr, m, ms, P, wb,
+                                            NULL)
+
+    def grads_s(wl=-1, wr=0, H=4, Hkv=2, ptrs=None, N=16, d=64, m=P, ms=0, wb=ws):
+        ptrs = ptrs or [P] * 8
+        return lib.fa_backward_grads_block_sparse(*ptrs, 1, H, Hkv, N, d, 0.125, wl, wr, m, ms,
+                                                  P, wb, NULL)
+
+    n_ptrs = {fwd_s: 5, bwd_s: 9, grads_s: 8}
+    for call in (fwd_s, bwd_s, grads_s):
+        assert call(wl=-2) == FA_ERR_ARG
+        assert call(m=NULL) == FA_ERR_NULL, call.__name__
+        assert call(ms=-1) == FA_ERR_ARG, call.__name__
+        assert call(m=NULL, ms=-1) == FA_ERR_NULL
+        assert call(m=PM, ms=-1) == FA_ERR_ARG  # a misaligned mask is fine, the stride is not
+        assert call(H=4, Hkv=3, m=NULL) == FA_ERR_SHAPE
+        assert call(d=80, m=NULL) == FA_ERR_HEADDIM
+        ptrs = [P] * n_ptrs[call]
+        ptrs[-1] = NULL
+        assert call(ptrs=ptrs, m=NULL) == FA_ERR_NULL
+        ptrs[-1] = PM
+        assert call(ptrs=ptrs, m=NULL) == FA_ERR_ALIGN  # tensor pointers are checked first
+        assert call(N=0, ptrs=[NULL] * n_ptrs[call], m=NULL, ms=-1) == FA_OK
+    assert bwd_s(wb=ws - 4, ms=-1) == FA_ERR_ARG
+    assert bwd_s(wb=ws - 4, ms=7) == FA_ERR_WORKSPACE
+    assert grads_s(wb=ws - 4, ms=7) == FA_ERR_WORKSPACE
+
+
 def test_fp8_workspace_size(lib):
     """Regions q8, qs, k8, ks, v8, vs, each rounded up to 256 bytes (T = ceil(N/64))."""
     # B=1, H=2, H_kv=1, N=100, d=64: 12800 + 1024 + 8192 + 256 + 8192 + 512
@@ -293,3 +334,5 @@ def test_python_binding_without_gpu_raises_cleanly(lib):
     k = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_forward_gqa(torch.zeros((1, 2, 4, 64), dtype=torch.bfloat16), k, k)
+    with pytest.raises(ValueError):
+        fa.fa_forward_block_sparse(q, q, q, torch.ones((1, 1), dtype=torch.uint8))

@@ -1,0 +1,209 @@
+"""GPU parity of block-sparse attention through the C ABI against the fp64
+oracle: blocks of 128 query rows x 128 keys whose mask byte is 0 are masked,
+on top of the window mask; a row that sees no key has O = 0, lse = -inf and
+no gradient."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_14_amd import (fa_backward_block_sparse, fa_backward_gqa,
+                                   fa_backward_grads_block_sparse, fa_backward_prep,
+                                   fa_backward_window, fa_forward_block_sparse, fa_forward_gqa,
+                                   fa_forward_window)
+from exact_io_aware_14_amd.inputs import (BLOCK_SPARSE_WORKLOADS, draw, draw_block_mask,
+                                          draw_segments, to_f64, workload_block_mask)
+from parity import LSE_MAX_ABS, check_grad, check_o, log, metrics, sample_heads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (B, H, H_kv, N, d): ragged lengths, grouped heads, the three head dimensions
+SHAPES = [(1, 2, 2, 300, 64), (1, 4, 2, 513, 128), (2, 2, 1, 200, 256), (1, 2, 1, 700, 128)]
+# no window, causal, a causal window crossing blocks, both sides bounded
+WINDOWS = [(-1, -1), (-1, 0), (150, 0), (40, 200)]
+# random half-dense masks with the diagonal kept; without it and with whole
+# block rows zeroed (rows that see nothing); packed segments
+PATTERNS = ["diag", "empty", "segments"]
+
+
+def _mask(pattern, B, H, N, seed):
+    if pattern == "diag":
+        return draw_block_mask(N, seed, 0.5, heads=(B, H))
+    if pattern == "empty":
+        return draw_block_mask(N, seed, 0.5, heads=(B, H), diagonal=False, empty_rows=1)
+    return draw_segments(N, seed, heads=(B, H))
+
+
+def check_lse_masked(lse, ref, what):
+    """lse against the oracle where a row sees a key; -inf exactly where it
+    sees none."""
+    assert not np.any(np.isnan(lse)), f"{what}: NaN in lse"
+    empty = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: empty rows differ"
+    assert np.all(np.isfinite(lse[~empty])), f"{what}: non-finite lse"
+    max_abs, _ = metrics(lse[~empty], ref[~empty])
+    log(f"  {what}: lse max_abs={max_abs:.3e} empty rows={int(empty.sum())}")
+    assert max_abs <= LSE_MAX_ABS, (what, max_abs)
+
+
+def _ids(cases):
+    return [f"{w[0]},{w[1]}" for w in cases]
+
+
+@pytest.mark.parametrize("pattern", PATTERNS)
+@pytest.mark.parametrize("window", WINDOWS, ids=_ids(WINDOWS))
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+def test_block_sparse_forward(shape, window, pattern):
+    B, H, Hkv, N, d = shape
+    q, k, v = draw((B, H, N, d), 700 + N, kv_heads=Hkv)
+    bm = _mask(pattern, B, H, N, 710 + N)
+    scale = 1.0 / math.sqrt(d)
+    log(f"case block-sparse forward {shape} {window} {pattern}")
+    o, lse = fa_forward_block_sparse(q.to(DEV), k.to(DEV), v.to(DEV), bm.to(DEV), *window,
+                                     scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            g = oracle.kv_head(h, H, Hkv)
+            ro, rl = oracle.forward_head(to_f64(q[b, h]), to_f64(k[b, g]), to_f64(v[b, g]),
+                                         scale, window, block_mask=bm[b, h].numpy())
+            what = f"{shape} {window} {pattern} b={b} h={h}"
+            empty = np.isneginf(rl)
+            assert np.all(o[b, h][empty] == 0.0), f"{what}: O of empty rows"
+            check_o(o[b, h], ro, what)
+            check_lse_masked(lse[b, h], rl, what)
+
+
+@pytest.mark.parametrize("pattern", PATTERNS)
+@pytest.mark.parametrize("window", WINDOWS, ids=_ids(WINDOWS))
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+def test_block_sparse_backward(shape, window, pattern):
+    B, H, Hkv, N, d = shape
+    q, k, v, do = draw((B, H, N, d), 800 + N, with_grad=True, kv_heads=Hkv)
+    bm = _mask(pattern, B, H, N, 810 + N)
+    scale = 1.0 / math.sqrt(d)
+    log(f"case block-sparse backward {shape} {window} {pattern}")
+    qd, kd, vd, dod, bmd = (x.to(DEV) for x in (q, k, v, do, bm))
+    o, lse = fa_forward_block_sparse(qd, kd, vd, bmd, *window, scale=scale)
+    dq, dk, dv = fa_backward_block_sparse(qd, kd, vd, o, dod, lse, bmd, *window, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, window,
+                                 block_mask=bm.numpy())
+    dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            check_grad(dq[b, h], rq[b, h], f"{shape} {window} {pattern} b={b} h={h} dQ")
+        for g in range(Hkv):
+            check_grad(dk[b, g], rk[b, g], f"{shape} {window} {pattern} b={b} kv={g} dK")
+            check_grad(dv[b, g], rv[b, g], f"{shape} {window} {pattern} b={b} kv={g} dV")
+    # rows that see no key have no gradient; keys no row sees neither
+    for b in range(B):
+        for h in range(H):
+            empty = ~np.isfinite(lse[b, h].cpu().numpy())
+            assert np.all(dq[b, h][empty] == 0.0)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_all_ones_mask_is_the_window_call(d):
+    """A mask of ones changes nothing: bitwise the results of the _window
+    calls (and, for no window, of the plain calls) on the same inputs."""
+    B, H, Hkv, N = 1, 4, 2, 333
+    q, k, v, do = (x.to(DEV) for x in draw((B, H, N, d), 90 + d, with_grad=True, kv_heads=Hkv))
+    nb = (N + 127) // 128
+    ones = torch.ones((nb, nb), dtype=torch.uint8, device=DEV)
+    for window in ((-1, 0), (100, 3), (-1, -1)):
+        log(f"case all-ones mask d={d} {window}")
+        o1, l1 = fa_forward_block_sparse(q, k, v, ones, *window)
+        g1 = fa_backward_block_sparse(q, k, v, o1, do, l1, ones, *window)
+        if window == (-1, -1):
+            o2, l2 = fa_forward_gqa(q, k, v, causal=False)
+            g2 = fa_backward_gqa(q, k, v, o2, do, l2, causal=False)
+        else:
+            o2, l2 = fa_forward_window(q, k, v, *window)
+            g2 = fa_backward_window(q, k, v, o2, do, l2, *window)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), window
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b), window
+
+
+def test_zero_mask_and_shared_mask():
+    """An all-zero mask: O = 0, lse = -inf and every gradient 0. A 2-D mask
+    (head stride 0) gives the results of the same mask repeated per head."""
+    B, H, Hkv, N, d = 2, 4, 2, 400, 128
+    q, k, v, do = (x.to(DEV) for x in draw((B, H, N, d), 97, with_grad=True, kv_heads=Hkv))
+    nb = (N + 127) // 128
+    log("case zero mask")
+    zero = torch.zeros((nb, nb), dtype=torch.uint8, device=DEV)
+    o, lse = fa_forward_block_sparse(q, k, v, zero, -1, 0)
+    grads = fa_backward_block_sparse(q, k, v, o, do, lse, zero, -1, 0)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    for g in grads:
+        assert torch.all(g == 0)
+    log("case shared mask")
+    shared = draw_block_mask(N, 98, 0.5).to(DEV)
+    per_head = shared.expand(B, H, nb, nb).contiguous()
+    o1, l1 = fa_forward_block_sparse(q, k, v, shared, -1, 0)
+    o2, l2 = fa_forward_block_sparse(q, k, v, per_head, -1, 0)
+    g1 = fa_backward_block_sparse(q, k, v, o1, do, l1, shared, -1, 0)
+    g2 = fa_backward_block_sparse(q, k, v, o2, do, l2, per_head, -1, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    # a bool mask is the same bytes
+    o3, l3 = fa_forward_block_sparse(q, k, v, shared.bool(), -1, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_block_sparse_stages_match_backward():
+    B, H, Hkv, N, d = 1, 4, 2, 600, 64
+    q, k, v, do = (x.to(DEV) for x in draw((B, H, N, d), 99, with_grad=True, kv_heads=Hkv))
+    bm = draw_block_mask(N, 100, 0.5, heads=(B, H), diagonal=False).to(DEV)
+    log("case block-sparse stages")
+    o, lse = fa_forward_block_sparse(q, k, v, bm, 300, 0)
+    ref = fa_backward_block_sparse(q, k, v, o, do, lse, bm, 300, 0)
+    ws = fa_backward_prep(o, do, lse)
+    got = fa_backward_grads_block_sparse(q, k, v, do, lse, ws, bm, 300, 0)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
+def test_block_sparse_full_size_workload():
+    """The block-sparse workload at full size: sampled heads of O and lse and
+    one head's gradients against the oracle."""
+    w = BLOCK_SPARSE_WORKLOADS[0]
+    window = (-1, 0) if w.causal else (-1, -1)
+    log(f"workload {w.name}")
+    q, k, v, do = draw(w.shape, w.seed, with_grad=True)
+    bm = workload_block_mask(w)
+    qd, kd, vd, dod, bmd = (x.to(DEV) for x in (q, k, v, do, bm))
+    o, lse = fa_forward_block_sparse(qd, kd, vd, bmd, *window, scale=w.scale)
+    dq, dk, dv = fa_backward_block_sparse(qd, kd, vd, o, dod, lse, bmd, *window, scale=w.scale)
+    torch.cuda.synchronize()
+    for x in (o, dq, dk, dv, lse):
+        assert torch.isfinite(x.float()).all()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    heads = sample_heads(w.B, w.H, 2, seed=w.seed)
+    for b, h in heads:
+        ro, rl = oracle.forward_head(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.scale,
+                                     window, block_mask=bm[b, h].numpy())
+        check_o(o[b, h], ro, f"{w.name} b={b} h={h}")
+        check_lse_masked(lse[b, h], rl, f"{w.name} b={b} h={h}")
+    b, h = heads[0]
+    rq, rk, rv = oracle.backward_head(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]),
+                                      to_f64(do[b, h]), w.scale, window,
+                                      block_mask=bm[b, h].numpy())
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check_grad(got[b, h].float().cpu().numpy(), ref, f"{w.name} b={b} h={h} {name}")
