@@ -297,56 +297,14 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   // each step, the tile (and, the first time, the key block) is in LDS for
   // every wave, and every wave is done with the previous step, whose stage
   // the loads of the next step overwrite.
-  //
-  // Block-sparse kernels: query tile t of query head jq lies in query block
-  // t/2 of that head's mask, in column kblk. The walk still passes one
-  // barrier per tile but loads and computes only the tiles of nonzero
-  // blocks; the flag of the tile after next is loaded while the current one
-  // is computed, so its latency is hidden.
-  auto advance = [&](int& jq, int& t) {  // the tile after (jq, t); false at the end
-    if (t + 1 < ntiles) {
-      ++t;
-      return true;
-    }
-    if (jq + 1 < p.group) {
-      ++jq;
-      t = t0;
-      return true;
-    }
-    return false;
-  };
-  static_assert(!SPARSE || (kKeyBlock == kMaskBlock && 2 * kTile == kMaskBlock),
-                "a dK/dV job is one key block of the mask, two tiles one query block");
-  const size_t qhead_first = (size_t)bh * p.group;  // the group's first query head
-  auto flag = [&](int jq, int t) { return mask_byte(p, qhead_first + jq, t >> 1, kblk); };
-  uint32_t on_cur = 1, on_nxt = 1, on_after = 0;  // flags: this tile, the next, the one after
-  if constexpr (SPARSE) {
-    int j = 0, t = t0;
-    on_cur = t0 < ntiles ? __builtin_amdgcn_readfirstlane(flag(0, t0)) : 0u;
-    on_nxt = t0 < ntiles && advance(j, t) ? __builtin_amdgcn_readfirstlane(flag(j, t)) : 0u;
-  }
   int step = 0;
   auto sync_fill = [&](int jq, int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if constexpr (SPARSE) {
-      int j1 = jq, t1 = t;
-      const bool has1 = advance(j1, t1);
-      int j2 = j1, t2 = t1;
-      on_after = has1 && advance(j2, t2) ? flag(j2, t2) : 0u;
-      if (has1 && on_nxt) fill(j1, t1, (step + 1) & 1);
-    } else {
-      if (t + 1 < ntiles)
-        fill(jq, t + 1, (step + 1) & 1);
-      else if (jq + 1 < p.group)
-        fill(jq + 1, t0, (step + 1) & 1);
-    }
-  };
-  auto rotate = [&]() {
-    if constexpr (SPARSE) {
-      on_cur = on_nxt;
-      on_nxt = __builtin_amdgcn_readfirstlane(on_after);
-    }
+    if (t + 1 < ntiles)
+      fill(jq, t + 1, (step + 1) & 1);
+    else if (jq + 1 < p.group)
+      fill(jq + 1, t0, (step + 1) & 1);
   };
   // Masked kernels: this wave's rows r0 .. r0+31 of tile t and its keys
   // kw0 .. kw0+31 all see each other for tiles tm1 .. tm2-1 (r0 >= kw0+31-wr
@@ -363,22 +321,75 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
     const int r0 = t * kTile + 32 * qh;
     return r0 + 31 >= kw0 - p.wr && r0 <= kw0 + 31 + p.wl;
   };
-  if (t0 < ntiles && (!SPARSE || on_cur)) fill(0, t0, 0);
-  for (int jq = 0; jq < p.group; ++jq) {
-    for (int t = t0; t < tm1; ++t, ++step) {
-      sync_fill(jq, t);
-      if ((!SPARSE || on_cur) && visible(t)) tile(t, step & 1, std::true_type());
-      rotate();
+  if constexpr (!SPARSE) {
+    if (t0 < ntiles) fill(0, t0, 0);
+    for (int jq = 0; jq < p.group; ++jq) {
+      for (int t = t0; t < tm1; ++t, ++step) {
+        sync_fill(jq, t);
+        if (visible(t)) tile(t, step & 1, std::true_type());
+      }
+      for (int t = tm1; t < tm2; ++t, ++step) {
+        sync_fill(jq, t);
+        tile(t, step & 1, std::false_type());
+      }
+      for (int t = tm2; t < ntiles; ++t, ++step) {
+        sync_fill(jq, t);
+        if (visible(t)) tile(t, step & 1, std::true_type());
+      }
     }
-    for (int t = tm1; t < tm2; ++t, ++step) {
-      sync_fill(jq, t);
-      if (!SPARSE || on_cur) tile(t, step & 1, std::false_type());
-      rotate();
-    }
-    for (int t = tm2; t < ntiles; ++t, ++step) {
-      sync_fill(jq, t);
-      if ((!SPARSE || on_cur) && visible(t)) tile(t, step & 1, std::true_type());
-      rotate();
+  } else {
+    // Block-sparse kernels: query tile t of query head jq lies in query
+    // block t/2 of that head's mask, in column kblk. The workgroup walks
+    // only the tiles of nonzero blocks, in the order above; each wave
+    // splits the walk at its own tm1, tm2 as above, so every wave passes
+    // the same barriers.
+    static_assert(kKeyBlock == kMaskBlock && 2 * kTile == kMaskBlock,
+                  "a dK/dV job is one key block of the mask, two tiles one query block");
+    const uint8_t* col0 = p.bmask + (size_t)bh * p.group * (size_t)p.bm_stride + kblk;
+    MaskScan scan;
+    scan.stride = (uint32_t)p.nbm;
+    scan.n = p.nbm;
+    int scan_head = 0;
+    scan.reset(col0, nullptr);
+    // the first tile at or after (jq, t) of a nonzero block; jq = group at the end
+    auto next_tile = [&](int& jq, int& t) {
+      while (jq < p.group) {
+        if (scan_head != jq) {
+          scan_head = jq;
+          scan.reset(col0 + (size_t)jq * (size_t)p.bm_stride, nullptr);
+        }
+        if (t < ntiles) {
+          uint32_t fl;
+          const int blk = scan.next(t >> 1, lane, &fl);
+          const int tn = blk == (t >> 1) ? t : 2 * blk;
+          if (tn < ntiles) {
+            t = tn;
+            return;
+          }
+        }
+        ++jq;
+        t = t0;
+      }
+    };
+    int cj = 0, ct = t0;
+    next_tile(cj, ct);
+    if (cj < p.group) fill(cj, ct, 0);
+    // one tile: load the next one of the walk, then compute (jq, t)
+    auto walk_step = [&](auto mask_c) {
+      int nj = cj, nt = ct + 1;
+      next_tile(nj, nt);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (nj < p.group) fill(nj, nt, (step + 1) & 1);
+      if (!decltype(mask_c)::value || visible(ct)) tile(ct, step & 1, mask_c);
+      cj = nj;
+      ct = nt;
+      ++step;
+    };
+    for (int jq = 0; jq < p.group; ++jq) {
+      while (cj == jq && ct < tm1) walk_step(std::true_type());
+      while (cj == jq && ct < tm2) walk_step(std::false_type());
+      while (cj == jq) walk_step(std::true_type());
     }
   }
 
@@ -543,43 +554,11 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
     }
   };
 
-  // Block-sparse kernels: key tile t lies in key block t/2; waves 0-3 hold
-  // query block 2*qblk of the head's mask, waves 4-7 block 2*qblk+1. A tile
-  // is loaded if either block is nonzero and computed by the waves of a
-  // nonzero one; bit h of a flag is block 2*qblk+h. The bytes of the tile
-  // after next are loaded while the current one is computed.
-  static_assert(!SPARSE || (kQBlock == 2 * kMaskBlock && 2 * kTile == kMaskBlock),
-                "a dQ job is two query blocks of the mask, two tiles one key block");
-  const int qbm = 2 * qblk;
-  const uint32_t my_bit = 1u << (wave >> 2);
-  uint32_t on_cur = 3, on_nxt = 3, after0 = 0, after1 = 0;
-  auto both = [&](uint32_t b0, uint32_t b1) {
-    return (__builtin_amdgcn_readfirstlane(b0) != 0 ? 1u : 0u) |
-           (__builtin_amdgcn_readfirstlane(b1) != 0 ? 2u : 0u);
-  };
-  if constexpr (SPARSE) {
-    on_cur = kt0 < ntiles ? both(mask_byte(p, bh, qbm, kt0 >> 1), mask_byte(p, bh, qbm + 1, kt0 >> 1))
-                          : 0u;
-    on_nxt = kt0 + 1 < ntiles ? both(mask_byte(p, bh, qbm, (kt0 + 1) >> 1),
-                                     mask_byte(p, bh, qbm + 1, (kt0 + 1) >> 1))
-                              : 0u;
-  }
   auto sync_fill = [&](int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if constexpr (SPARSE) {
-      after0 = t + 2 < ntiles ? mask_byte(p, bh, qbm, (t + 2) >> 1) : 0u;
-      after1 = t + 2 < ntiles ? mask_byte(p, bh, qbm + 1, (t + 2) >> 1) : 0u;
-    }
-    if (t + 1 < ntiles && (!SPARSE || on_nxt)) fill(t + 1);
+    if (t + 1 < ntiles) fill(t + 1);
   };
-  auto rotate = [&]() {
-    if constexpr (SPARSE) {
-      on_cur = on_nxt;
-      on_nxt = both(after0, after1);
-    }
-  };
-  auto mine = [&]() { return !SPARSE || (on_cur & my_bit) != 0; };
   // Key tile t shows all of its keys to all of this wave's rows for tiles
   // tm1 .. tm2-1 (t*64 >= wave_last-wl and t*64+63 <= qw0+wr); the visible
   // tiles before and after cross a window edge (masked). Three loops (every
@@ -592,21 +571,57 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   }
   if (qw0 >= N) tm2 = tm1;  // no rows: every tile is skipped
   auto visible = [&](int t) { return t >= wt0 && t < wt1; };
-  if (!SPARSE || on_cur) fill(kt0);
-  for (int t = kt0; t < tm1; ++t) {
-    sync_fill(t);
-    if (mine() && visible(t)) tile(t, std::true_type());
-    rotate();
-  }
-  for (int t = tm1; t < tm2; ++t) {
-    sync_fill(t);
-    if (mine()) tile(t, std::false_type());
-    rotate();
-  }
-  for (int t = tm2; t < ntiles; ++t) {
-    sync_fill(t);
-    if (mine() && visible(t)) tile(t, std::true_type());
-    rotate();
+  if constexpr (!SPARSE) {
+    fill(kt0);
+    for (int t = kt0; t < tm1; ++t) {
+      sync_fill(t);
+      if (visible(t)) tile(t, std::true_type());
+    }
+    for (int t = tm1; t < tm2; ++t) {
+      sync_fill(t);
+      tile(t, std::false_type());
+    }
+    for (int t = tm2; t < ntiles; ++t) {
+      sync_fill(t);
+      if (visible(t)) tile(t, std::true_type());
+    }
+  } else {
+    // Block-sparse kernels: key tile t lies in key block t/2; waves 0-3
+    // hold query block 2*qblk of the head's mask, waves 4-7 block 2*qblk+1.
+    // The workgroup walks the tiles where either block is nonzero (their
+    // stage is t & 1 as above, so tiles of one block keep alternating
+    // stages and a skipped block skips two); a wave computes those where
+    // its own block is nonzero.
+    static_assert(kQBlock == 2 * kMaskBlock && 2 * kTile == kMaskBlock,
+                  "a dQ job is two query blocks of the mask, two tiles one key block");
+    const int qbm = 2 * qblk;
+    const uint8_t* row0 = p.bmask + (size_t)bh * (size_t)p.bm_stride + (size_t)qbm * p.nbm;
+    MaskScan scan;
+    scan.stride = 1;
+    scan.n = p.nbm;
+    scan.reset(row0, qbm + 1 < p.nbm ? row0 + p.nbm : nullptr);
+    const uint32_t my_bit = 1u << (wave >> 2);
+    // the first tile >= t where either block is nonzero (else ntiles), and its flags
+    auto next_tile = [&](int t, uint32_t* fl) {
+      const int blk = scan.next(t >> 1, lane, fl);
+      return blk == (t >> 1) ? t : min(2 * blk, ntiles);
+    };
+    uint32_t cf;
+    int t = next_tile(kt0, &cf);
+    if (t < ntiles) fill(t);
+    auto walk_step = [&](auto mask_c) {
+      uint32_t nf;
+      const int tn = next_tile(t + 1, &nf);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tn < ntiles) fill(tn);
+      if ((cf & my_bit) != 0 && (!decltype(mask_c)::value || visible(t))) tile(t, mask_c);
+      t = tn;
+      cf = nf;
+    };
+    while (t < tm1) walk_step(std::true_type());
+    while (t < tm2) walk_step(std::false_type());
+    while (t < ntiles) walk_step(std::true_type());
   }
 
   if (myq < N) store_rows<D>(p.dq + (head + myq) * D, dqacc, p.scale, half);

@@ -156,13 +156,6 @@ BwdParams make_params(const BwdArgs& a) {
   return p;
 }
 
-// Byte (qb, kb) of the block mask of query head h; 0 for a query block past
-// the last (the second half of a 256-row dQ job at the end of a head).
-__device__ __forceinline__ uint32_t mask_byte(const BwdParams& p, size_t h, int qb, int kb) {
-  if (qb >= p.nbm) return 0u;
-  return p.bmask[h * (size_t)p.bm_stride + (size_t)qb * p.nbm + kb];
-}
-
 }  // namespace
 
 // the grads launch at d = 256 (fa_bwd_w.hip)

@@ -228,53 +228,14 @@ __device__ __forceinline__ void dkdv_job_w(const BwdParams& p, int bh, int kblk,
     }
   };
 
-  // Block-sparse kernels: query tile t of query head jq lies in query block
-  // t/4 of that head's mask, in column kblk; only tiles of nonzero blocks
-  // are loaded and computed (the walk as at d = 128).
-  static_assert(!SPARSE || (kKeyBlockW == kMaskBlock && 4 * kQTileW == kMaskBlock),
-                "a dK/dV job is one key block of the mask, four tiles one query block");
-  auto advance = [&](int& jq, int& t) {  // the tile after (jq, t); false at the end
-    if (t + 1 < ntiles) {
-      ++t;
-      return true;
-    }
-    if (jq + 1 < p.group) {
-      ++jq;
-      t = t0;
-      return true;
-    }
-    return false;
-  };
-  const size_t qhead_first = (size_t)bh * p.group;  // the group's first query head
-  auto flag = [&](int jq, int t) { return mask_byte(p, qhead_first + jq, t >> 2, kblk); };
-  uint32_t on_cur = 1, on_nxt = 1, on_after = 0;  // flags: this tile, the next, the one after
-  if constexpr (SPARSE) {
-    int j = 0, t = t0;
-    on_cur = t0 < ntiles ? __builtin_amdgcn_readfirstlane(flag(0, t0)) : 0u;
-    on_nxt = t0 < ntiles && advance(j, t) ? __builtin_amdgcn_readfirstlane(flag(j, t)) : 0u;
-  }
   int step = 0;
   auto sync_fill = [&](int jq, int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if constexpr (SPARSE) {
-      int j1 = jq, t1 = t;
-      const bool has1 = advance(j1, t1);
-      int j2 = j1, t2 = t1;
-      on_after = has1 && advance(j2, t2) ? flag(j2, t2) : 0u;
-      if (has1 && on_nxt) fill(j1, t1, (step + 1) & 1);
-    } else {
-      if (t + 1 < ntiles)
-        fill(jq, t + 1, (step + 1) & 1);
-      else if (jq + 1 < p.group)
-        fill(jq + 1, t0, (step + 1) & 1);
-    }
-  };
-  auto rotate = [&]() {
-    if constexpr (SPARSE) {
-      on_cur = on_nxt;
-      on_nxt = __builtin_amdgcn_readfirstlane(on_after);
-    }
+    if (t + 1 < ntiles)
+      fill(jq, t + 1, (step + 1) & 1);
+    else if (jq + 1 < p.group)
+      fill(jq + 1, t0, (step + 1) & 1);
   };
   // this wave's keys kw0 .. kw0+31 and the rows r0 .. r0+31 of tile t all
   // see each other for tiles tm1 .. tm2-1; the visible tiles before and
@@ -288,22 +249,71 @@ __device__ __forceinline__ void dkdv_job_w(const BwdParams& p, int bh, int kblk,
     const int r0 = t * kQTileW;
     return r0 + 31 >= kw0 - p.wr && r0 <= kw0 + 31 + p.wl;
   };
-  if (t0 < ntiles && (!SPARSE || on_cur)) fill(0, t0, 0);
-  for (int jq = 0; jq < p.group; ++jq) {
-    for (int t = t0; t < tm1; ++t, ++step) {
-      sync_fill(jq, t);
-      if ((!SPARSE || on_cur) && visible(t)) tile(t, step & 1, std::true_type());
-      rotate();
+  if constexpr (!SPARSE) {
+    if (t0 < ntiles) fill(0, t0, 0);
+    for (int jq = 0; jq < p.group; ++jq) {
+      for (int t = t0; t < tm1; ++t, ++step) {
+        sync_fill(jq, t);
+        if (visible(t)) tile(t, step & 1, std::true_type());
+      }
+      for (int t = tm1; t < tm2; ++t, ++step) {
+        sync_fill(jq, t);
+        tile(t, step & 1, std::false_type());
+      }
+      for (int t = tm2; t < ntiles; ++t, ++step) {
+        sync_fill(jq, t);
+        if (visible(t)) tile(t, step & 1, std::true_type());
+      }
     }
-    for (int t = tm1; t < tm2; ++t, ++step) {
-      sync_fill(jq, t);
-      if (!SPARSE || on_cur) tile(t, step & 1, std::false_type());
-      rotate();
-    }
-    for (int t = tm2; t < ntiles; ++t, ++step) {
-      sync_fill(jq, t);
-      if ((!SPARSE || on_cur) && visible(t)) tile(t, step & 1, std::true_type());
-      rotate();
+  } else {
+    // Block-sparse kernels: query tile t of query head jq lies in query
+    // block t/4 of that head's mask, in column kblk; the walk over the
+    // tiles of nonzero blocks is that of the d = 128 job.
+    static_assert(kKeyBlockW == kMaskBlock && 4 * kQTileW == kMaskBlock,
+                  "a dK/dV job is one key block of the mask, four tiles one query block");
+    const uint8_t* col0 = p.bmask + (size_t)bh * p.group * (size_t)p.bm_stride + kblk;
+    MaskScan scan;
+    scan.stride = (uint32_t)p.nbm;
+    scan.n = p.nbm;
+    int scan_head = 0;
+    scan.reset(col0, nullptr);
+    auto next_tile = [&](int& jq, int& t) {  // first tile at or after (jq, t); jq = group: none
+      while (jq < p.group) {
+        if (scan_head != jq) {
+          scan_head = jq;
+          scan.reset(col0 + (size_t)jq * (size_t)p.bm_stride, nullptr);
+        }
+        if (t < ntiles) {
+          uint32_t fl;
+          const int blk = scan.next(t >> 2, lane, &fl);
+          const int tn = blk == (t >> 2) ? t : 4 * blk;
+          if (tn < ntiles) {
+            t = tn;
+            return;
+          }
+        }
+        ++jq;
+        t = t0;
+      }
+    };
+    int cj = 0, ct = t0;
+    next_tile(cj, ct);
+    if (cj < p.group) fill(cj, ct, 0);
+    auto walk_step = [&](auto mask_c) {
+      int nj = cj, nt = ct + 1;
+      next_tile(nj, nt);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (nj < p.group) fill(nj, nt, (step + 1) & 1);
+      if (!decltype(mask_c)::value || visible(ct)) tile(ct, step & 1, mask_c);
+      cj = nj;
+      ct = nt;
+      ++step;
+    };
+    for (int jq = 0; jq < p.group; ++jq) {
+      while (cj == jq && ct < tm1) walk_step(std::true_type());
+      while (cj == jq && ct < tm2) walk_step(std::false_type());
+      while (cj == jq) walk_step(std::true_type());
     }
   }
   if (mykey < N) {
@@ -440,30 +450,10 @@ __device__ __forceinline__ void dq_job_w(const BwdParams& p, int bh, int qblk,
       }
   };
 
-  // Block-sparse kernels: the job is query block qblk of the head's mask;
-  // key tile t lies in key block t/2. Only tiles of nonzero blocks are
-  // loaded and computed; the flag of the tile after next is loaded while
-  // the current one is computed.
-  static_assert(!SPARSE || (kQBlockW == kMaskBlock && 2 * kKTileW == kMaskBlock),
-                "a dQ job is one query block of the mask, two tiles one key block");
-  uint32_t on_cur = 1, on_nxt = 1, on_after = 0;
-  if constexpr (SPARSE) {
-    on_cur = kt0 < ntiles ? __builtin_amdgcn_readfirstlane(mask_byte(p, bh, qblk, kt0 >> 1)) : 0u;
-    on_nxt = kt0 + 1 < ntiles
-                 ? __builtin_amdgcn_readfirstlane(mask_byte(p, bh, qblk, (kt0 + 1) >> 1))
-                 : 0u;
-  }
   auto sync_fill = [&](int t) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if constexpr (SPARSE) on_after = t + 2 < ntiles ? mask_byte(p, bh, qblk, (t + 2) >> 1) : 0u;
-    if (t + 1 < ntiles && (!SPARSE || on_nxt)) fill(t + 1);
-  };
-  auto rotate = [&]() {
-    if constexpr (SPARSE) {
-      on_cur = on_nxt;
-      on_nxt = __builtin_amdgcn_readfirstlane(on_after);
-    }
+    if (t + 1 < ntiles) fill(t + 1);
   };
   int tm1 = kt0, tm2 = wt1;
   if (CAUSAL) {
@@ -472,21 +462,49 @@ __device__ __forceinline__ void dq_job_w(const BwdParams& p, int bh, int qblk,
   }
   if (qw0 >= N) tm2 = tm1;
   auto visible = [&](int t) { return t >= wt0 && t < wt1; };
-  if (!SPARSE || on_cur) fill(kt0);
-  for (int t = kt0; t < tm1; ++t) {
-    sync_fill(t);
-    if ((!SPARSE || on_cur) && visible(t)) tile(t, std::true_type());
-    rotate();
-  }
-  for (int t = tm1; t < tm2; ++t) {
-    sync_fill(t);
-    if (!SPARSE || on_cur) tile(t, std::false_type());
-    rotate();
-  }
-  for (int t = tm2; t < ntiles; ++t) {
-    sync_fill(t);
-    if ((!SPARSE || on_cur) && visible(t)) tile(t, std::true_type());
-    rotate();
+  if constexpr (!SPARSE) {
+    fill(kt0);
+    for (int t = kt0; t < tm1; ++t) {
+      sync_fill(t);
+      if (visible(t)) tile(t, std::true_type());
+    }
+    for (int t = tm1; t < tm2; ++t) {
+      sync_fill(t);
+      tile(t, std::false_type());
+    }
+    for (int t = tm2; t < ntiles; ++t) {
+      sync_fill(t);
+      if (visible(t)) tile(t, std::true_type());
+    }
+  } else {
+    // Block-sparse kernels: the job is query block qblk of the head's mask;
+    // key tile t lies in key block t/2. The workgroup walks the tiles of
+    // nonzero blocks (stage t & 1 still alternates along the walk: each
+    // block is two tiles).
+    static_assert(kQBlockW == kMaskBlock && 2 * kKTileW == kMaskBlock,
+                  "a dQ job is one query block of the mask, two tiles one key block");
+    MaskScan scan;
+    scan.stride = 1;
+    scan.n = p.nbm;
+    scan.reset(p.bmask + (size_t)bh * (size_t)p.bm_stride + (size_t)qblk * p.nbm, nullptr);
+    auto next_tile = [&](int t) {  // the first tile >= t of a nonzero block, else ntiles
+      uint32_t fl;
+      const int blk = scan.next(t >> 1, lane, &fl);
+      return blk == (t >> 1) ? t : min(2 * blk, ntiles);
+    };
+    int t = next_tile(kt0);
+    if (t < ntiles) fill(t);
+    auto walk_step = [&](auto mask_c) {
+      const int tn = next_tile(t + 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tn < ntiles) fill(tn);
+      if (!decltype(mask_c)::value || visible(t)) tile(t, mask_c);
+      t = tn;
+    };
+    while (t < tm1) walk_step(std::true_type());
+    while (t < tm2) walk_step(std::false_type());
+    while (t < ntiles) walk_step(std::true_type());
   }
 
   if (myq < N) store_rows<D>(p.dq + (head + myq) * D, dqacc, p.scale, half);

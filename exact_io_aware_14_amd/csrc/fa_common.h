@@ -224,6 +224,50 @@ __device__ __forceinline__ bool in_window(int x, int lo, uint32_t count) {
   return (uint32_t)(x - lo) < count;
 }
 
+// Scan of the nonzero entries of a block-sparse mask along one row (stride
+// 1) or one column (stride nb): entries a[i * stride], i < n, and optionally
+// a second sequence b alike (nullptr: none). It reads 64 entries at a time,
+// one byte per lane, and keeps them as two 64-bit ballots, so the search is
+// scalar; every wave of a workgroup scans the same bytes and finds the same
+// entries.
+struct MaskScan {
+  const uint8_t* a;
+  const uint8_t* b;
+  uint32_t stride;
+  int n;
+  int chunk;  // entries 64*chunk .. 64*chunk+63 are in bits_a, bits_b
+  uint64_t bits_a, bits_b;
+
+  __device__ __forceinline__ void reset(const uint8_t* a_, const uint8_t* b_) {
+    a = a_;
+    b = b_;
+    chunk = -1;
+  }
+  // The first i' >= i where a or b is nonzero, else n; *flags gets bit 0 for
+  // a[i'] != 0 and bit 1 for b[i'] != 0.
+  __device__ __forceinline__ int next(int i, int lane, uint32_t* flags) {
+    while (i < n) {
+      const int c = i >> 6;
+      if (c != chunk) {
+        chunk = c;
+        const int j = (c << 6) + lane;
+        const size_t off = (size_t)j * stride;
+        bits_a = __ballot(j < n && a[off] != 0);
+        bits_b = b == nullptr ? 0ull : __ballot(j < n && b[off] != 0);
+      }
+      const uint64_t ra = bits_a >> (i & 63), rb = bits_b >> (i & 63);
+      if ((ra | rb) != 0) {
+        const int k = __builtin_ctzll(ra | rb);
+        *flags = (uint32_t)((ra >> k) & 1) | (uint32_t)(((rb >> k) & 1) << 1);
+        return i + k;
+      }
+      i = (c + 1) << 6;
+    }
+    *flags = 0;
+    return n;
+  }
+};
+
 // Integer division rounding toward -infinity / +infinity (b > 0).
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
 __device__ __forceinline__ int ceil_div(int a, int b) { return -floor_div(-a, b); }

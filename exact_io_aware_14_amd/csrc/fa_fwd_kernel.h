@@ -337,20 +337,6 @@ void fwd_kernel(FwdParams p) {
     l_run += ls0 + ls1;
   };
 
-  // ---- block-sparse kernels: tile t lies in key block t/2 of the mask row
-  // of this query block; the workgroup still walks every tile (one barrier
-  // each) but loads and computes only those of nonzero blocks. The flag of
-  // tile t+2 is loaded while tile t is computed, so its latency is hidden.
-  const uint8_t* bm_row = nullptr;
-  uint32_t on_cur = 1, on_nxt = 1;  // flags of the current and the next tile
-  if constexpr (SPARSE) {
-    bm_row = p.bmask + (size_t)bh * (size_t)p.bm_stride + (size_t)qb * p.nbm;
-    on_cur = __builtin_amdgcn_readfirstlane((uint32_t)bm_row[t_first >> 1]);
-    on_nxt = t_first + 1 < t_end
-                 ? __builtin_amdgcn_readfirstlane((uint32_t)bm_row[(t_first + 1) >> 1])
-                 : 0u;
-  }
-
   // ---- tiles. K and V of tile t+1 load while tile t is computed: one
   // barrier per tile, after which tile t is in LDS for every wave and every
   // wave is done with tile t-1, whose stage the loads of tile t+1 overwrite.
@@ -359,31 +345,65 @@ void fwd_kernel(FwdParams p) {
                   unsigned char* vn) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    uint32_t on_after = 0;  // SPARSE: flag of tile t+2, loaded before the tile loads
-    if constexpr (SPARSE) {
-      if (t + 2 < t_end) on_after = bm_row[(t + 2) >> 1];
-    }
-    if (t + 1 < t_end && (!SPARSE || on_nxt)) {
+    if (t + 1 < t_end) {
       fill_tile(kg, t + 1, kn, fk);
       fill_tile(vg, t + 1, vn, fk);
     }
-    if ((!SPARSE || on_cur) && t >= wt_first && t < wt_end) {
+    if (t >= wt_first && t < wt_end) {
       qk(kc);
       softmax(t);
       pv(vc);
     }
-    if constexpr (SPARSE) {
-      on_cur = on_nxt;
-      on_nxt = __builtin_amdgcn_readfirstlane(on_after);
-    }
   };
-  if (!SPARSE || on_cur) {
+  if constexpr (!SPARSE) {
     fill_tile(kg, t_first, k0, fk);
     fill_tile(vg, t_first, v0, fk);
-  }
-  for (int t = t_first; t < t_end; t += 2) {
-    step(t, k0, v0, k1, v1);
-    if (t + 1 < t_end) step(t + 1, k1, v1, k0, v0);
+    for (int t = t_first; t < t_end; t += 2) {
+      step(t, k0, v0, k1, v1);
+      if (t + 1 < t_end) step(t + 1, k1, v1, k0, v0);
+    }
+  } else {
+    // Block-sparse kernels: tile t lies in key block t/2 of the mask row of
+    // this query block; the workgroup walks only the tiles of nonzero
+    // blocks, in order, with the same double buffering (tn: the tile after
+    // t, loaded while t is computed).
+    MaskScan scan;
+    scan.stride = 1;
+    scan.n = p.nbm;
+    scan.reset(p.bmask + (size_t)bh * (size_t)p.bm_stride + (size_t)qb * p.nbm, nullptr);
+    auto next_tile = [&](int t) {  // the first tile >= t of a nonzero block, else t_end
+      uint32_t fl;
+      const int blk = scan.next(t >> 1, lane, &fl);
+      return blk == (t >> 1) ? t : min(2 * blk, t_end);
+    };
+    auto step_to = [&](int t, int tn, const unsigned char* kc, const unsigned char* vc,
+                       unsigned char* kn, unsigned char* vn) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tn < t_end) {
+        fill_tile(kg, tn, kn, fk);
+        fill_tile(vg, tn, vn, fk);
+      }
+      if (t >= wt_first && t < wt_end) {
+        qk(kc);
+        softmax(t);
+        pv(vc);
+      }
+    };
+    int t = next_tile(t_first);
+    if (t < t_end) {
+      fill_tile(kg, t, k0, fk);
+      fill_tile(vg, t, v0, fk);
+    }
+    while (t < t_end) {
+      int tn = next_tile(t + 1);
+      step_to(t, tn, k0, v0, k1, v1);
+      t = tn;
+      if (t >= t_end) break;
+      tn = next_tile(t + 1);
+      step_to(t, tn, k1, v1, k0, v0);
+      t = tn;
+    }
   }
 
   // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2
