@@ -207,3 +207,85 @@ def test_block_sparse_full_size_workload():
                                       block_mask=bm[b, h].numpy())
     for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
         check_grad(got[b, h].float().cpu().numpy(), ref, f"{w.name} b={b} h={h} {name}")
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_block_sparse_long_rows_and_columns(d):
+    """N = 8300: 65 mask blocks per row and column, so every walk reads its
+    mask in two 64-block pieces. Sampled rows of O and lse of both heads
+    and the gradients of the whole problem against the oracle, causal and a
+    window."""
+    B, H, Hkv, N = 1, 2, 1, 8300
+    q, k, v, do = draw((B, H, N, d), 120 + d, with_grad=True, kv_heads=Hkv)
+    bm = draw_block_mask(N, 121 + d, 0.3, heads=(B, H))
+    bm[0, 1, :, 64] = 1  # the last block column, seen by every row of head 1
+    scale = 1.0 / math.sqrt(d)
+    rows = np.array(sorted(set(range(0, 200)) | set(range(8100, N)) |
+                           set(np.random.default_rng(d).integers(0, N, 300).tolist())))
+    qd, kd, vd, dod, bmd = (x.to(DEV) for x in (q, k, v, do, bm))
+    for window in ((-1, 0), (3000, 100)):
+        log(f"case block-sparse long d={d} {window}")
+        o, lse = fa_forward_block_sparse(qd, kd, vd, bmd, *window, scale=scale)
+        dq, dk, dv = fa_backward_block_sparse(qd, kd, vd, o, dod, lse, bmd, *window, scale=scale)
+        torch.cuda.synchronize()
+        on, ln = o.float().cpu().numpy(), lse.cpu().numpy()
+        for h in range(H):
+            ro, rl = oracle.forward_head(to_f64(q[0, h]), to_f64(k[0, 0]), to_f64(v[0, 0]), scale,
+                                         window, rows=rows, block_mask=bm[0, h].numpy())
+            check_o(on[0, h][rows], ro, f"long d={d} {window} h={h}")
+            check_lse_masked(ln[0, h][rows], rl, f"long d={d} {window} h={h}")
+        rq, rk, rv = oracle.backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, window,
+                                     block_mask=bm.numpy())
+        for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            got = got.float().cpu().numpy()
+            for h in range(got.shape[1]):
+                check_grad(got[0, h], ref[0, h], f"long d={d} {window} h={h} {name}")
+
+
+def test_block_sparse_graph_replays_match_eager():
+    """Block-sparse calls captured into a HIP graph replay like eager calls,
+    also with new mask contents written between replays (the kernels read
+    the mask at run time)."""
+    shape = (1, 4, 600, 128)
+    B, H, N, d = shape
+    nb = (N + 127) // 128
+    q, k, v, do = (torch.empty(shape, dtype=torch.bfloat16, device=DEV) for _ in range(4))
+    bm = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    from exact_io_aware_14_amd import fa_backward_workspace_size
+    ws = torch.empty(fa_backward_workspace_size(*shape), dtype=torch.uint8, device=DEV)
+
+    def step():
+        fa_forward_block_sparse(q, k, v, bm, -1, 0, o=o, lse=lse)
+        fa_backward_block_sparse(q, k, v, o, do, lse, bm, -1, 0, dq=dq, dk=dk, dv=dv,
+                                 workspace=ws)
+
+    for x, y in zip((q, k, v, do), draw(shape, 130, with_grad=True)):
+        x.copy_(y)
+    bm.copy_(draw_block_mask(N, 131, 0.5, heads=(B, H)))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        log(f"case block-sparse graph replay {r}")
+        for x, y in zip((q, k, v, do), draw(shape, 132 + r, with_grad=True)):
+            x.copy_(y)
+        bm.copy_(draw_block_mask(N, 140 + r, 0.5, heads=(B, H), diagonal=r != 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (o, lse, dq, dk, dv)]
+        eo, el = fa_forward_block_sparse(q, k, v, bm, -1, 0)
+        eg = fa_backward_block_sparse(q, k, v, eo, do, el, bm, -1, 0)
+        torch.cuda.synchronize()
+        for a, b in zip(got, (eo, el, *eg)):
+            assert torch.equal(a, b), f"replay {r}"
