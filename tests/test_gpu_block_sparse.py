@@ -289,3 +289,29 @@ def test_block_sparse_graph_replays_match_eager():
         torch.cuda.synchronize()
         for a, b in zip(got, (eo, el, *eg)):
             assert torch.equal(a, b), f"replay {r}"
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_block_sparse_writes_every_output(d):
+    """Outputs preallocated as NaN: every element is written, including the
+    rows that see no key (O = 0, lse = -inf, dQ = 0) and the keys no row
+    sees (dK = dV = 0)."""
+    B, H, Hkv, N = 1, 2, 1, 450
+    q, k, v, do = (x.to(DEV) for x in draw((B, H, N, d), 150 + d, with_grad=True, kv_heads=Hkv))
+    bm = draw_block_mask(N, 151 + d, 0.4, heads=(B, H), diagonal=False, empty_rows=1).to(DEV)
+    bm[:, :, :, 2] = 0  # key block 2 is seen by no row
+    nan = float("nan")
+    o = torch.full_like(q, nan)
+    lse = torch.full((B, H, N), nan, device=DEV)
+    dq, dk, dv = torch.full_like(q, nan), torch.full_like(k, nan), torch.full_like(v, nan)
+    log(f"case block-sparse poisoned outputs d={d}")
+    fa_forward_block_sparse(q, k, v, bm, -1, -1, o=o, lse=lse)
+    fa_backward_block_sparse(q, k, v, o, do, lse, bm, -1, -1, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert not torch.isnan(lse).any()
+    for x in (o, dq, dk, dv):
+        assert torch.isfinite(x.float()).all()
+    empty = torch.isneginf(lse)
+    assert empty.any()
+    assert torch.all(o[empty] == 0) and torch.all(dq[empty] == 0)
+    assert torch.all(dk[:, :, 256:384] == 0) and torch.all(dv[:, :, 256:384] == 0)
