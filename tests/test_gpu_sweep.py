@@ -74,3 +74,61 @@ def test_sweep_forward_backward(case):
         for g in range(Hkv):
             check_grad(dk[b, g], rk[b, g], f"{case} b={b} kv={g} dK")
             check_grad(dv[b, g], rv[b, g], f"{case} b={b} kv={g} dV")
+
+
+def _draw_sparse_cases(n, seed):
+    """The same draw, plus a block mask: density, diagonal kept or not, and
+    one mask shared by all heads or one per query head."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for B, H, Hkv, N, d, window in _draw_cases(n, seed):
+        density = float(rng.choice([0.2, 0.5, 0.8]))
+        diagonal = bool(rng.random() < 0.5)
+        shared = bool(rng.random() < 0.3)
+        # lengths of several mask blocks half the time
+        N = N if rng.random() < 0.5 else int(rng.integers(300, 1300))
+        cases.append((B, H, Hkv, N, d, window, density, diagonal, shared))
+    return cases
+
+
+SPARSE_CASES = _draw_sparse_cases(16, seed=20261204)
+
+
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=[f"{i}-{c}" for i, c in enumerate(SPARSE_CASES)])
+def test_sweep_block_sparse(case):
+    from exact_io_aware_14_amd import fa_backward_block_sparse, fa_forward_block_sparse
+    from exact_io_aware_14_amd.inputs import draw_block_mask
+
+    B, H, Hkv, N, d, window, density, diagonal, shared = case
+    seed = 9000 + 31 * N + d + H
+    q, k, v, do = draw((B, H, N, d), seed, with_grad=True, kv_heads=Hkv)
+    bm = draw_block_mask(N, seed + 1, density, heads=() if shared else (B, H), diagonal=diagonal)
+    scale = 1.0 / math.sqrt(d)
+    log(f"case sparse sweep B={B} H={H} Hkv={Hkv} N={N} d={d} window={window} "
+        f"density={density} diagonal={diagonal} shared={shared}")
+    qd, kd, vd, dod, bmd = (x.to(DEV) for x in (q, k, v, do, bm))
+    o, lse = fa_forward_block_sparse(qd, kd, vd, bmd, *window, scale=scale)
+    dq, dk, dv = fa_backward_block_sparse(qd, kd, vd, o, dod, lse, bmd, *window, scale=scale)
+    torch.cuda.synchronize()
+    bm_np = bm.numpy()
+    rq, rk, rv = oracle.backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, window,
+                                 block_mask=bm_np)
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            g = oracle.kv_head(h, H, Hkv)
+            hm = bm_np if shared else bm_np[b, h]
+            ro, rl = oracle.forward_head(to_f64(q[b, h]), to_f64(k[b, g]), to_f64(v[b, g]), scale,
+                                         window, block_mask=hm)
+            what = f"{case} b={b} h={h}"
+            empty = np.isneginf(rl)
+            assert np.array_equal(np.isneginf(lse[b, h]), empty), what
+            assert np.all(o[b, h][empty] == 0.0), what
+            check_o(o[b, h], ro, what)
+            if (~empty).any():
+                check_lse(lse[b, h][~empty], rl[~empty], what)
+            check_grad(dq[b, h], rq[b, h], what + " dQ")
+        for g in range(Hkv):
+            check_grad(dk[b, g], rk[b, g], f"{case} b={b} kv={g} dK")
+            check_grad(dv[b, g], rv[b, g], f"{case} b={b} kv={g} dV")
