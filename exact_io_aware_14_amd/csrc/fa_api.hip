@@ -2,6 +2,7 @@
 // caller's stream. Declarations and the contract are in include/fa.h.
 #include "fa.h"
 
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -46,9 +47,14 @@ int check_ptrs(const void* const* ptrs, int n) {
 // The block mask of the block-sparse calls: any address (bytes), a
 // nonnegative head stride. nullptr stands for "no mask" inside the library,
 // so the block-sparse calls check it here.
-int check_mask(const uint8_t* mask, long long stride) {
+int check_mask(const uint8_t* mask, long long stride, int B, int H, int N) {
   if (mask == nullptr) return FA_ERR_NULL;
   if (stride < 0) return FA_ERR_ARG;
+  // the last head's mask must be addressable: (B*H - 1) * stride + nb*nb bytes
+  // past the pointer in 64 bits (the kernels index it with size_t)
+  const long long nb = (N + fa::kMaskBlock - 1) / fa::kMaskBlock;
+  const long long heads = (long long)B * H;
+  if (stride > 0 && heads > 1 && heads - 1 > (LLONG_MAX - nb * nb) / stride) return FA_ERR_ARG;
   return FA_OK;
 }
 
@@ -66,7 +72,7 @@ int forward_common(const void* q, const void* k, const void* v, void* o, float* 
   const void* ptrs[5] = {q, k, v, o, lse};
   st = check_ptrs(ptrs, 5);
   if (st != FA_OK) return st;
-  if (sparse && (st = check_mask(mask, mask_stride)) != FA_OK) return st;
+  if (sparse && (st = check_mask(mask, mask_stride, B, H, N)) != FA_OK) return st;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, wl, wr, stream, Hkv, mask, mask_stride};
   hipError_t e = f32 ? fa::launch_forward_f32(a) : fa::launch_forward_bf16(a);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -83,7 +89,7 @@ int grads_common(const void* q, const void* k, const void* v, const void* dout,
   const void* ptrs[8] = {q, k, v, dout, lse, dq, dk, dv};
   st = check_ptrs(ptrs, 8);
   if (st != FA_OK) return st;
-  if (sparse && (st = check_mask(mask, mask_stride)) != FA_OK) return st;
+  if (sparse && (st = check_mask(mask, mask_stride, B, H, N)) != FA_OK) return st;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
   fa::BwdArgs a{q, k, v, nullptr, dout, lse, dq, dk, dv,
                 static_cast<float*>(const_cast<void*>(workspace)), B, H, N, d, scale, wl, wr,
@@ -102,7 +108,7 @@ int backward_common(const void* q, const void* k, const void* v, const void* o,
   const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
   st = check_ptrs(ptrs, 9);
   if (st != FA_OK) return st;
-  if (sparse && (st = check_mask(mask, mask_stride)) != FA_OK) return st;
+  if (sparse && (st = check_mask(mask, mask_stride, B, H, N)) != FA_OK) return st;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d)) return FA_ERR_WORKSPACE;
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace),
                 B, H, N, d, scale, wl, wr, stream, Hkv, mask, mask_stride};

@@ -239,7 +239,8 @@ int fa_backward_grads_window(const void* q, const void* k, const void* v, const 
  * Inputs are bf16 as in fa_forward_window / fa_backward_window, whose
  * argument rules, workspace and results these calls share; a NULL
  * block_mask returns FA_ERR_NULL (checked after the tensor pointers), a
- * negative stride FA_ERR_ARG. The mask takes no alignment. The backward
+ * negative stride, or one so large that (B*H - 1) * stride + nb*nb
+ * overflows 64 bits, FA_ERR_ARG. The mask takes no alignment. The backward
  * calls take the lse of the forward call with the same mask.
  */
 int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,

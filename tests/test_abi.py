@@ -263,6 +263,8 @@ def test_block_sparse_validation(lib):
         ptrs[-1] = PM
         assert call(ptrs=ptrs, m=NULL) == FA_ERR_ALIGN  # tensor pointers are checked first
         assert call(N=0, ptrs=[NULL] * n_ptrs[call], m=NULL, ms=-1) == FA_OK
+    for call in (fwd_s, bwd_s, grads_s):
+        assert call(ms=2 ** 62) == FA_ERR_ARG  # (B*H - 1) * stride overflows 64 bits
     assert bwd_s(wb=ws - 4, ms=-1) == FA_ERR_ARG
     assert bwd_s(wb=ws - 4, ms=7) == FA_ERR_WORKSPACE
     assert grads_s(wb=ws - 4, ms=7) == FA_ERR_WORKSPACE
