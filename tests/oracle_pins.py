@@ -560,6 +560,67 @@ def pin_block_diagonal_segments():
             _close(g[seg], gs, 1e-13, f"segment {s} gradients")
 
 
+# ---------------------------------------------------------------- row chunks and row subsets
+# forward_head forms the scores of at most 512 query rows at a time and can
+# compute a subset of the rows. Every GPU comparison at N > 512 goes through
+# these two paths, so they are pinned at a length that takes three chunks
+# (512 + 512 + 76 rows), with every kind of mask, against torch fp64
+# attention whose masks are built from tril / triu / kron alone.
+
+def _torch_masked_attention(q, k, v, scale, keep):
+    t = [torch.tensor(x, dtype=torch.float64) for x in (q, k, v)]
+    sc = (t[0] @ t[1].T * scale).masked_fill(~keep, -math.inf)
+    return (torch.softmax(sc, dim=-1) @ t[2]).numpy(), torch.logsumexp(sc, dim=-1).numpy()
+
+
+def _kron_block_keep(bm, n):
+    """Element mask of a block mask by a Kronecker product with 128 x 128 ones."""
+    return torch.tensor(np.kron(np.asarray(bm) != 0, np.ones((BLOCK, BLOCK), dtype=bool))[:n, :n])
+
+
+def pin_row_chunks_vs_torch():
+    rng = np.random.default_rng(47)
+    n, d, scale = 1100, 4, 0.8
+    nb = -(-n // BLOCK)
+    subset = np.concatenate([[1099, 0, 512, 511, 1024, 1023, 700], rng.permutation(n)[:650],
+                             [5, 5]])  # unsorted, across every chunk edge, one row twice
+    cases = [(True, _torch_window_mask(n, -1, 0), None),
+             ((300, 50), _torch_window_mask(n, 300, 50), None),
+             ((-1, 7), _torch_window_mask(n, -1, 7), None),
+             ((600, -1), _torch_window_mask(n, 600, -1), None)]
+    bm = _random_block_mask(rng, nb)  # diagonal blocks kept: no row is empty
+    cases.append((True, _torch_window_mask(n, -1, 0) & _kron_block_keep(bm, n), bm))
+    cases.append((False, _kron_block_keep(bm.T, n), bm.T.copy()))
+    for causal, keep, mask in cases:
+        q, k, v = _rand_head(rng, n, d)
+        ro, rl = _torch_masked_attention(q, k, v, scale, keep)
+        what = f"n={n} mask={causal} block={mask is not None}"
+        o, lse = A.forward_head(q, k, v, scale, causal, block_mask=mask)
+        _close(o, ro, 1e-12, f"chunked O vs torch {what}")
+        _close(lse, rl, 1e-12, f"chunked lse vs torch {what}")
+        o_s, lse_s = A.forward_head(q, k, v, scale, causal, rows=subset, block_mask=mask)
+        _close(o_s, ro[subset], 1e-12, f"row subset O vs torch {what}")
+        _close(lse_s, rl[subset], 1e-12, f"row subset lse vs torch {what}")
+
+
+def pin_row_chunks_zero_queries():
+    # closed form across chunks: zero queries see the mean of their visible
+    # values, lse = ln(count), for a causal mask and a window
+    rng = np.random.default_rng(48)
+    n, d = 1100, 3
+    v = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    q = np.zeros((n, d))
+    rows = np.array([1099, 3, 600, 1030, 512])
+    for left, right in ((-1, 0), (100, 20)):
+        o, lse = A.forward_head(q, k, v, 1.0, (left, right), rows=rows)
+        for r, i in enumerate(rows):
+            lo = 0 if left < 0 else max(0, i - left)
+            hi = min(n - 1, i + right)
+            _close(o[r], v[lo:hi + 1].mean(axis=0), 1e-12, f"zero-query mean row {i}")
+            _close(lse[r], math.log(hi - lo + 1), 1e-12, f"zero-query lse row {i}")
+
+
 # ---------------------------------------------------------------- FP8 with incoherent processing
 
 def pin_fp8_e4m3_golden():
@@ -723,7 +784,8 @@ ALL_PINS = [pin_golden_forward, pin_golden_backward, pin_vs_torch_sdpa,
             pin_gqa_vs_autograd, pin_gqa_finite_differences, pin_window_special_cases,
             pin_window_vs_torch, pin_window_brute_force, pin_block_mask_all_ones,
             pin_block_mask_vs_torch, pin_block_mask_brute_force, pin_block_mask_empty_rows,
-            pin_block_diagonal_segments, pin_fp8_e4m3_golden,
+            pin_block_diagonal_segments, pin_row_chunks_vs_torch, pin_row_chunks_zero_queries,
+            pin_fp8_e4m3_golden,
             pin_fp8_e4m3_grid, pin_fp8_scales, pin_fp8_v_blocks, pin_fp8_forward_golden,
             pin_fp8_pv_error_bound, pin_fp8_hadamard, pin_fp8_rotation_is_exact, pin_fp8_error_bound,
             pin_fp8_incoherence_lowers_error]

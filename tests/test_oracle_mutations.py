@@ -75,6 +75,30 @@ def _fwd_transposed_p(q, k, v, scale, causal, rows=None, block_mask=None):
     return o[ids], lse
 
 
+def _fwd_chunk_variant(kind):
+    """forward_head with the row chunks or the row subset mishandled."""
+    def fwd(q, k, v, scale, causal, rows=None, block_mask=None):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+        if kind == "rows_ignored":
+            rows = np.arange(rows.shape[0])
+        out = np.zeros((rows.shape[0], v.shape[1]))
+        lse = np.zeros(rows.shape[0])
+        for start in range(0, rows.shape[0], A._ROW_CHUNK):
+            ids = rows[start:start + A._ROW_CHUNK]
+            # the mistake: row ids counted from the start of the chunk
+            mask_ids = ids - start if kind == "chunk_local_ids" else ids
+            s = A._apply_block_mask(A._scores(q[ids], k, scale, mask_ids, causal), mask_ids,
+                                    block_mask)
+            l_rows = A._row_softmax_stats(s)
+            p = np.exp(s - np.where(np.isfinite(l_rows), l_rows, 0.0)[:, None])
+            p = np.where(np.isfinite(l_rows)[:, None], p, 0.0)
+            out[start:start + ids.shape[0]] = p @ v
+            lse[start:start + ids.shape[0]] = l_rows
+        return out, lse
+    return fwd
+
+
 def _kv_head_modulo(h, heads, kv_heads):
     return h % kv_heads
 
@@ -242,6 +266,8 @@ MUTATIONS = {
     "bwd_dv_untransposed": ("backward_head", _bwd_variant("dv_no_transpose")),
     "bwd_dq_scale_dropped": ("backward_head", _bwd_variant("dq_no_scale")),
     "fwd_p_transposed": ("forward_head", _fwd_transposed_p),
+    "fwd_chunk_local_row_ids": ("forward_head", _fwd_chunk_variant("chunk_local_ids")),
+    "fwd_rows_argument_ignored": ("forward_head", _fwd_chunk_variant("rows_ignored")),
     "gqa_head_map_modulo": ("kv_head", _kv_head_modulo),
     "gqa_head_map_reversed": ("kv_head", _kv_head_reversed),
     "gqa_grads_overwritten": ("backward", _backward_not_summed),
