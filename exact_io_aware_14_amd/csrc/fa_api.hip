@@ -58,6 +58,12 @@ int check_mask(const uint8_t* mask, long long stride, int B, int H, int N) {
   return FA_OK;
 }
 
+// A window bound of N - 1 or more cuts no key of an N-key head, so it is the
+// same mask as no bound on that side (-1). Mapping it to -1 here keeps every
+// bound the kernels see below N, so that a row or key index plus a bound
+// stays within int whatever the caller passes (INT_MAX included).
+int norm_bound(int w, int N) { return w >= N - 1 ? -1 : w; }
+
 bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d) {
   return ws != nullptr && aligned16(ws) && bytes >= fa_backward_workspace_size(B, H, N, d);
 }
@@ -69,6 +75,8 @@ int forward_common(const void* q, const void* k, const void* v, void* o, float* 
   bool empty = false;
   int st = check_common(B, H, Hkv, N, d, scale, wl, wr, &empty);
   if (st != FA_OK || empty) return st;
+  wl = norm_bound(wl, N);
+  wr = norm_bound(wr, N);
   const void* ptrs[5] = {q, k, v, o, lse};
   st = check_ptrs(ptrs, 5);
   if (st != FA_OK) return st;
@@ -86,6 +94,8 @@ int grads_common(const void* q, const void* k, const void* v, const void* dout,
   bool empty = false;
   int st = check_common(B, H, Hkv, N, d, scale, wl, wr, &empty);
   if (st != FA_OK || empty) return st;
+  wl = norm_bound(wl, N);
+  wr = norm_bound(wr, N);
   const void* ptrs[8] = {q, k, v, dout, lse, dq, dk, dv};
   st = check_ptrs(ptrs, 8);
   if (st != FA_OK) return st;
@@ -105,6 +115,8 @@ int backward_common(const void* q, const void* k, const void* v, const void* o,
   bool empty = false;
   int st = check_common(B, H, Hkv, N, d, scale, wl, wr, &empty);
   if (st != FA_OK || empty) return st;
+  wl = norm_bound(wl, N);
+  wr = norm_bound(wr, N);
   const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
   st = check_ptrs(ptrs, 9);
   if (st != FA_OK) return st;

@@ -192,7 +192,9 @@ int fa_backward_grads_gqa(const void* q, const void* k, const void* v, const voi
  *     (window_right < 0 or j <= i + window_right),
  * -1 meaning no bound on that side. (-1, 0) is the causal mask, (-1, -1) no
  * mask, (W-1, 0) a causal window of W keys. Bounds below -1 return
- * FA_ERR_ARG. Every row sees at least its own key whenever both bounds are
+ * FA_ERR_ARG. A bound of N-1 or more cuts no key and is the same mask as
+ * -1 (any int is accepted, INT_MAX included; the results are bitwise those
+ * of -1). Every row sees at least its own key whenever both bounds are
  * >= 0, and key 0 or key N-1 otherwise, so no row is empty. Query tiles and
  * key tiles that no visible pair touches are skipped, like the tiles above
  * the diagonal under the causal mask.

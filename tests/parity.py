@@ -2,7 +2,14 @@
 
 Tolerances (HIP path vs the fp64 oracle on identical bf16 inputs):
   O          max abs error <= 1e-2 and relative L2 error <= 5e-3
-  dQ, dK, dV relative L2 error <= 2e-2
+  dQ, dK, dV relative L2 error <= 2e-2 over the head, and for every row r
+             |g_r - ref_r| <= 3e-2 * max(|ref_r|, rms) (L2 norms of rows,
+             rms = the root mean square row norm of the head's reference);
+             a bf16 emulation of the backward arithmetic (P and dS rounded
+             as MFMA operands, outputs rounded) gives worst rows of 4-5e-3
+             at scale 1/sqrt(d) and 1.1e-2 at scale 0.4, while a zeroed row
+             scores about 1 and a row missing one 64-key tile out of 16384
+             about 6e-2
   lse        max abs error <= 1e-3 (lse never passes through bf16; the
              expected error is ~1e-5, set by fp32 sums and bf16 rounding of P)
 
@@ -25,6 +32,7 @@ import numpy as np
 O_MAX_ABS = 1e-2
 O_REL_L2 = 5e-3
 GRAD_REL_L2 = 2e-2
+GRAD_ROW_REL = 3e-2
 LSE_MAX_ABS = 1e-3
 
 
@@ -74,11 +82,27 @@ def check_lse(lse, ref, what):
     assert max_abs <= LSE_MAX_ABS, (what, max_abs)
 
 
+def row_errors(g, ref):
+    """Per-row L2 error of g against ref, relative to max(row norm, rms row norm)."""
+    g = np.asarray(g, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+    ref = np.asarray(ref, dtype=np.float64).reshape(g.shape)
+    if ref.size == 0:
+        return np.zeros(0)
+    rown = np.linalg.norm(ref, axis=1)
+    rms = float(np.linalg.norm(ref)) / np.sqrt(ref.shape[0])
+    floor = np.maximum(rown, rms)
+    err = np.linalg.norm(g - ref, axis=1)
+    return np.where(floor > 0, err / np.where(floor > 0, floor, 1.0), err)
+
+
 def check_grad(g, ref, what):
     assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
     max_abs, rel = metrics(g, ref)
-    log(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    rows = row_errors(g, ref)
+    worst = float(rows.max()) if rows.size else 0.0
+    log(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} worst row={worst:.3e}")
     assert rel <= GRAD_REL_L2, (what, max_abs, rel)
+    assert worst <= GRAD_ROW_REL, (what, "row", int(np.argmax(rows)), worst)
 
 
 def sample_rows(n, seed, edge=256, rand=512):

@@ -226,6 +226,14 @@ def test_window_validation(lib):
         assert call(N=0, ptrs=[NULL] * n_ptrs[call]) == FA_OK
     assert bwd_w(wb=ws - 4) == FA_ERR_WORKSPACE
     assert grads_w(wb=ws - 4) == FA_ERR_WORKSPACE
+    # any bound >= -1 is valid, INT_MAX included (a bound of N - 1 or more is
+    # no bound): validation goes on to the pointers
+    big = 2 ** 31 - 1
+    for call in (fwd_w, bwd_w, grads_w):
+        for wl, wr in ((big, 0), (-1, big), (big, big), (big - 5, 16)):
+            ptrs = [P] * n_ptrs[call]
+            ptrs[-1] = PM
+            assert call(wl=wl, wr=wr, ptrs=ptrs) == FA_ERR_ALIGN, (call.__name__, wl, wr)
 
 
 def test_block_sparse_validation(lib):

@@ -98,6 +98,35 @@ def test_window_causal_and_full_are_the_plain_calls():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_window_bounds_past_the_sequence(d):
+    """A bound of N - 1 or more (INT_MAX included) cuts no key: bitwise the
+    results of no bound on that side, forward and backward; N - 2 still cuts
+    and matches the oracle."""
+    B, H, Hkv, N = 1, 2, 1, 200
+    big = 2 ** 31 - 1
+    q, k, v, do = (x.to(DEV) for x in draw((B, H, N, d), 64 + d, with_grad=True, kv_heads=Hkv))
+    for window, same in (((-1, big), (-1, -1)), ((big, 0), (-1, 0)), ((big, big), (-1, -1)),
+                         ((N - 1, N - 1), (-1, -1)), ((big - N, 0), (-1, 0)),
+                         ((0, big), (0, -1))):
+        log(f"case window bounds {window} as {same} d={d}")
+        o1, l1 = fa_forward_window(q, k, v, *window)
+        o2, l2 = fa_forward_window(q, k, v, *same)
+        g1 = fa_backward_window(q, k, v, o1, do, l1, *window)
+        g2 = fa_backward_window(q, k, v, o2, do, l2, *same)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), window
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b), window
+    scale = d ** -0.5
+    o, lse = fa_forward_window(q, k, v, N - 2, 0, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.forward_head(to_f64(q[0, 0].cpu()), to_f64(k[0, 0].cpu()),
+                                 to_f64(v[0, 0].cpu()), scale, (N - 2, 0))
+    check_o(o[0, 0].float().cpu().numpy(), ro, f"window ({N - 2}, 0) d={d}")
+    check_lse(lse[0, 0].cpu().numpy(), rl, f"window ({N - 2}, 0) d={d}")
+
+
 def test_window_stages_match_backward():
     B, H, Hkv, N, d = 1, 4, 2, 300, 64
     q, k, v, do = (x.to(DEV) for x in draw((B, H, N, d), 63, with_grad=True, kv_heads=Hkv))
