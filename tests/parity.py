@@ -9,7 +9,10 @@ Tolerances (HIP path vs the fp64 oracle on identical bf16 inputs):
              as MFMA operands, outputs rounded) gives worst rows of 4-5e-3
              at scale 1/sqrt(d) and 1.1e-2 at scale 0.4, while a zeroed row
              scores about 1 and a row missing one 64-key tile out of 16384
-             about 6e-2
+             about 6e-2. dQ rows get an additive allowance on top
+             (dq_allowance): D_i is formed from the stored bf16 O, and
+             dQ_i depends on D_i through -scale * sum_j P_ij K_j, which is
+             large on short causal rows, whose dQ may itself be small
   lse        max abs error <= 1e-3 (lse never passes through bf16; the
              expected error is ~1e-5, set by fp32 sums and bf16 rounding of P)
 
@@ -28,6 +31,8 @@ from __future__ import annotations
 import sys
 
 import numpy as np
+
+import oracle
 
 O_MAX_ABS = 1e-2
 O_REL_L2 = 5e-3
@@ -82,8 +87,9 @@ def check_lse(lse, ref, what):
     assert max_abs <= LSE_MAX_ABS, (what, max_abs)
 
 
-def row_errors(g, ref):
-    """Per-row L2 error of g against ref, relative to max(row norm, rms row norm)."""
+def row_errors(g, ref, allow=None):
+    """Per-row L2 error of g against ref, less the row's allowance (if any),
+    relative to max(row norm, rms row norm)."""
     g = np.asarray(g, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
     ref = np.asarray(ref, dtype=np.float64).reshape(g.shape)
     if ref.size == 0:
@@ -92,13 +98,48 @@ def row_errors(g, ref):
     rms = float(np.linalg.norm(ref)) / np.sqrt(ref.shape[0])
     floor = np.maximum(rown, rms)
     err = np.linalg.norm(g - ref, axis=1)
+    if allow is not None:
+        err = np.maximum(err - np.asarray(allow, dtype=np.float64).reshape(-1), 0.0)
     return np.where(floor > 0, err / np.where(floor > 0, floor, 1.0), err)
 
 
-def check_grad(g, ref, what):
+def dq_allowance(q, k, v, do, scale, causal, block_mask=None):
+    """Per-row bound (L2) on how far dQ_i moves because D_i = sum_k dO_ik O_ik
+    is formed from the forward's stored O rather than the exact one, for one
+    head, from the oracle alone. dQ_i is linear in D_i with slope
+    -scale * sum_j P_ij K_j = -scale * (attention of q over values K)_i, and
+    the stored O differs from the exact one by its bf16 rounding (u |O_ik|)
+    plus that of the probabilities it was formed from (u sum_j P_ij |V_jk|),
+    u = 2^-8, so |delta D_i| <= u sum_k |dO_ik| (|O_ik| + sum_j P_ij |V_jk|)."""
+    o, _ = oracle.forward_head(q, k, v, scale, causal, block_mask=block_mask)
+    pav, _ = oracle.forward_head(q, k, np.abs(v), scale, causal, block_mask=block_mask)
+    pk, _ = oracle.forward_head(q, k, k, scale, causal, block_mask=block_mask)
+    dmax = BF16_U * np.sum(np.abs(do) * (np.abs(o) + pav), axis=1)
+    return abs(scale) * dmax * np.linalg.norm(pk, axis=1)
+
+
+def dq_allowances(q, k, v, do, scale, causal, block_mask=None):
+    """dq_allowance for every query head of [B,H,N,d] q, do and [B,Hkv,N,d]
+    k, v (query head h reads K/V head h / (H / Hkv)); block_mask as for
+    oracle.backward. Returns [B, H, N]."""
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    out = np.zeros(q.shape[:3])
+    for b in range(B):
+        for h in range(H):
+            g = oracle.kv_head(h, H, Hkv)
+            bm = None if block_mask is None else (
+                np.asarray(block_mask) if np.ndim(block_mask) == 2 else np.asarray(block_mask)[b, h])
+            out[b, h] = dq_allowance(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal, bm)
+    return out
+
+
+def check_grad(g, ref, what, allow=None):
+    """Head-level relative L2 and the per-row bound; `allow`: an additive
+    per-row allowance (dq_allowance for dQ)."""
     assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
     max_abs, rel = metrics(g, ref)
-    rows = row_errors(g, ref)
+    rows = row_errors(g, ref, allow)
     worst = float(rows.max()) if rows.size else 0.0
     log(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} worst row={worst:.3e}")
     assert rel <= GRAD_REL_L2, (what, max_abs, rel)

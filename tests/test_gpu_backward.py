@@ -12,7 +12,7 @@ import oracle
 from exact_io_aware_14_amd import (fa_backward, fa_backward_grads, fa_backward_prep,
                                    fa_backward_workspace_size, fa_forward)
 from exact_io_aware_14_amd.inputs import WORKLOADS, draw, to_f64
-from parity import check_grad, check_o, log, sample_heads
+from parity import check_grad, check_o, dq_allowance, log, sample_heads
 
 pytestmark = pytest.mark.gpu
 
@@ -31,9 +31,9 @@ def _compare_heads(q, k, v, do, scale, causal, heads, outs, what):
     _, _, dq, dk, dv = outs
     dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
     for b, h in heads:
-        rq, rk, rv = oracle.backward_head(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]),
-                                          to_f64(do[b, h]), scale, causal)
-        check_grad(dq[b, h], rq, f"{what} b={b} h={h} dQ")
+        args = (to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), to_f64(do[b, h]), scale, causal)
+        rq, rk, rv = oracle.backward_head(*args)
+        check_grad(dq[b, h], rq, f"{what} b={b} h={h} dQ", allow=dq_allowance(*args))
         check_grad(dk[b, h], rk, f"{what} b={b} h={h} dK")
         check_grad(dv[b, h], rv, f"{what} b={b} h={h} dV")
 

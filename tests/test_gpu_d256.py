@@ -16,7 +16,7 @@ from exact_io_aware_14_amd import (fa_backward, fa_backward_grads, fa_backward_p
                                    fa_backward_window, fa_forward, fa_forward_f32,
                                    fa_forward_window)
 from exact_io_aware_14_amd.inputs import D256_WORKLOADS, draw, to_f64
-from parity import check_grad, check_lse, check_o, log, sample_heads
+from parity import check_grad, check_lse, check_o, dq_allowance, dq_allowances, log, sample_heads
 
 pytestmark = pytest.mark.gpu
 
@@ -64,11 +64,13 @@ def test_d256_backward(case):
     o, lse = fa_forward_window(qd, kd, vd, wl, wr, scale=scale)
     dq, dk, dv = fa_backward_window(qd, kd, vd, o, dod, lse, wl, wr, scale=scale)
     torch.cuda.synchronize()
-    rq, rk, rv = oracle.backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, (wl, wr))
+    args = (to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, (wl, wr))
+    rq, rk, rv = oracle.backward(*args)
+    aq = dq_allowances(*args)
     dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
     for b in range(B):
         for h in range(H):
-            check_grad(dq[b, h], rq[b, h], f"{case} b={b} h={h} dQ")
+            check_grad(dq[b, h], rq[b, h], f"{case} b={b} h={h} dQ", allow=aq[b, h])
         for g in range(Hkv):
             check_grad(dk[b, g], rk[b, g], f"{case} b={b} kv={g} dK")
             check_grad(dv[b, g], rv[b, g], f"{case} b={b} kv={g} dV")
@@ -125,10 +127,12 @@ def test_d256_full_size_workload():
         check_o(o[b, h], ro, f"{w.name} b={b} h={h}")
         check_lse(lse[b, h].cpu().numpy(), rl, f"{w.name} b={b} h={h}")
     b, h = 3, 7
-    rq, rk, rv = oracle.backward_head(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]),
-                                      to_f64(do[b, h]), w.scale, True)
-    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
-        check_grad(got[b, h].float().cpu().numpy(), ref, f"{w.name} b={b} h={h} {name}")
+    args = (to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), to_f64(do[b, h]), w.scale, True)
+    rq, rk, rv = oracle.backward_head(*args)
+    aq = dq_allowance(*args)
+    for name, got, ref, al in (("dQ", dq, rq, aq), ("dK", dk, rk, None), ("dV", dv, rv, None)):
+        check_grad(got[b, h].float().cpu().numpy(), ref, f"{w.name} b={b} h={h} {name}",
+                   allow=al)
 
 
 def test_d256_writes_every_output_and_is_deterministic():
