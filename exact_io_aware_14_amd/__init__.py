@@ -14,7 +14,7 @@ import ctypes
 import os
 
 __all__ = ["FAError", "fa_forward", "fa_forward_gqa", "fa_forward_window", "fa_forward_f32",
-           "fa_backward", "fa_backward_gqa", "fa_backward_window", "fa_backward_prep",
+           "fa_backward", "fa_backward_noalloc", "fa_backward_gqa", "fa_backward_window", "fa_backward_prep",
            "fa_backward_grads", "fa_backward_grads_gqa", "fa_backward_grads_window",
            "fa_forward_block_sparse", "fa_backward_block_sparse",
            "fa_backward_grads_block_sparse", "MASK_BLOCK",
@@ -80,6 +80,10 @@ def library():
         lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
                                     vp, sz, vp]
         lib.fa_backward.restype = i
+        if hasattr(lib, "fa_backward_noalloc"):
+            lib.fa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f,
+                                                i, vp]
+            lib.fa_backward_noalloc.restype = i
         lib.fa_backward_prep.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
         lib.fa_backward_prep.restype = i
         lib.fa_backward_grads.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
@@ -251,6 +255,24 @@ def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=Non
                                _stream(stream, q, k, v, o, dout, lse, dq, dk, dv, ws))
     if st != 0:
         raise FAError(st, "fa_backward")
+    return dq, dk, dv
+
+
+def fa_backward_noalloc(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None,
+                        dv=None, stream=None):
+    """fa_backward with the row terms in the library's static scratch instead
+    of a workspace (see fa_backward_noalloc in fa.h). The library allocates
+    nothing; pass dq, dk, dv to keep this call free of torch allocations too."""
+    shape, dev, (dq, dk, dv) = _bwd_check(
+        q, (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)), lse,
+        (("dq", dq), ("dk", dk), ("dv", dv)))
+    scale = shape[3] ** -0.5 if scale is None else scale
+    st = library().fa_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), *shape, float(scale),
+                                       int(bool(causal)),
+                                       _stream(stream, q, k, v, o, dout, lse, dq, dk, dv))
+    if st != 0:
+        raise FAError(st, "fa_backward_noalloc")
     return dq, dk, dv
 
 

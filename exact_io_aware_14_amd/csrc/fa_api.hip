@@ -6,7 +6,22 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fa_launch.h"
+
+// Static scratch of fa_backward_noalloc: the row terms of the backward pass
+// (D, then lse * log2(e), 2 x [B,H,N] fp32) for callers that cannot
+// allocate. At most kScratchRows rows (B * H * N): 16 MiB on every GPU the
+// library runs on, held until the process ends. Host code never passes this
+// name to a kernel (on the host it is only a stand-in): it uses the device
+// address that scratch_address() looks up per device.
+namespace {
+constexpr long long kScratchRows = 2LL << 20;
+constexpr size_t kScratchBytes = 2 * (size_t)kScratchRows * sizeof(float);
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -175,6 +190,30 @@ int fp8_forward(const void* workspace, size_t workspace_bytes, void* o, float* l
   return fa::launch_forward_fp8(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Device address of `scratch` on the current device. Each GPU holds its own
+// copy of the array at its own address; it is looked up once per device,
+// with that device current, and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+        return FA_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FA_OK;
+}
+
 // The causal flag of the entry points without a window: 1 is the window
 // (-1, 0), 0 no mask; anything else is FA_ERR_ARG, reported as an invalid
 // bound.
@@ -256,6 +295,26 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o,
   return backward_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale,
                          causal_left(causal), causal_right(causal), workspace, workspace_bytes,
                          stream);
+}
+
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                        int H, int N, int d, float scale, int causal, hipStream_t stream) {
+  bool empty = false;
+  const int wl = causal_left(causal), wr = causal_right(causal);
+  int st = check_common(B, H, H, N, d, scale, wl, wr, &empty);
+  if (st != FA_OK || empty) return st;
+  const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
+  st = check_ptrs(ptrs, 9);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * N > kScratchRows) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != FA_OK) return st;
+  // the row-term launch writes every row the grads launch reads: nothing in
+  // the scratch needs clearing, whatever an earlier call left there
+  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale, wl, wr, ws,
+                         kScratchBytes, stream);
 }
 
 int fa_forward_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -367,6 +426,9 @@ const char* fa_strerror(int status) {
              "signs +1 or -1, block-mask head stride >= 0";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case FA_ERR_SCRATCH:
+      return "problem too large for the static scratch of fa_backward_noalloc "
+             "(B*H*N at most 2097152)";
     default: return "unknown status";
   }
 }

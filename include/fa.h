@@ -28,7 +28,9 @@
  *   nothing and returns FA_OK; null pointers are then accepted.
  * - Calls are asynchronous: they enqueue kernels on `stream` (NULL means the
  *   null stream) and return. The library never allocates, frees or
- *   synchronises and keeps no mutable global state, so it is reentrant.
+ *   synchronises and keeps no mutable global state, so it is reentrant
+ *   (fa_backward_noalloc alone shares one static scratch array per GPU
+ *   between its calls, see there).
  *   A call only launches kernels (no allocation, no memset), so it can be
  *   captured into a HIP graph on `stream` and replayed; a replay reads the
  *   buffers' contents at replay time. The FP8 sign vector, read from host
@@ -66,7 +68,8 @@ typedef enum {
     FA_ERR_ARG = 5,       /* causal not 0/1, a window bound below -1, scale not finite,
                              an FP8 sign not +1/-1, or a negative block-mask head stride */
     FA_ERR_WORKSPACE = 6, /* workspace missing, misaligned or too small */
-    FA_ERR_HIP = 7        /* the HIP runtime reported an error at launch */
+    FA_ERR_HIP = 7,       /* the HIP runtime reported an error at launch */
+    FA_ERR_SCRATCH = 8    /* fa_backward_noalloc: B*H*N above its static scratch (2097152) */
 } fa_status;
 
 /*
@@ -126,6 +129,28 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, int causal,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_backward without the workspace arguments, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The row terms go to a static scratch
+ * array inside the library instead: 16 MiB on each GPU the library runs on,
+ * taken when the library is loaded and held until the process ends, enough
+ * for B*H*N <= 2097152 rows; larger problems return FA_ERR_SCRATCH before any
+ * HIP call. The call allocates nothing; on its first use on a device it looks
+ * up that device's address of the array (the device current at the call,
+ * which `stream` must belong to). Results are bitwise those of fa_backward.
+ * Every call on one GPU uses the same array, and the row-term launch
+ * rewrites every row the gradient launch reads, so nothing needs clearing
+ * between calls; but calls whose kernels can overlap on one GPU (on
+ * different streams, from different threads, graph replays in flight) race
+ * on it and must be ordered by the caller. Arguments and other errors as
+ * for fa_backward.
+ */
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, float scale, int causal,
+                        hipStream_t stream);
 
 /*
  * First stage of fa_backward: for every row, D_i = sum_k dout_ik O_ik and

@@ -16,7 +16,7 @@ HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROO
            if f.endswith(".h")]
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_ARG, \
-    FA_ERR_WORKSPACE, FA_ERR_HIP = range(8)
+    FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCRATCH = range(9)
 
 
 def declared_functions():
@@ -43,14 +43,15 @@ def test_every_declared_symbol_is_exported(lib):
             "fa_forward_window", "fa_backward_window", "fa_backward_grads_window",
             "fa_forward_fp8", "fa_fp8_prepare", "fa_forward_fp8_prepared",
             "fa_forward_fp8_workspace_size", "fa_forward_block_sparse",
-            "fa_backward_block_sparse", "fa_backward_grads_block_sparse"} <= set(names)
+            "fa_backward_block_sparse", "fa_backward_grads_block_sparse",
+            "fa_backward_noalloc"} <= set(names)
     raw = ctypes.CDLL(fa.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), f"{name} declared in include/ but not exported"
 
 
 def test_strerror(lib):
-    for code in range(8):
+    for code in range(9):
         s = fa.fa_strerror(code)
         assert isinstance(s, str) and s
     assert fa.fa_strerror(0) == "success"
@@ -194,6 +195,29 @@ def test_grouped_validation(lib):
         assert fwd_g(ptrs=ptrs) == FA_ERR_NULL
     assert bwd_g(wb=ws - 1) == FA_ERR_WORKSPACE
     assert grads_g(wb=ws - 1) == FA_ERR_WORKSPACE
+
+
+def test_noalloc_validation(lib):
+    """fa_backward_noalloc: the checks of fa_backward, then the size of its
+    static scratch (B*H*N at most 2^21 rows), all before any HIP call."""
+    def call(B=1, H=1, N=16, d=64, causal=0, ptrs=None):
+        ptrs = ptrs or [P] * 9
+        return lib.fa_backward_noalloc(*ptrs, B, H, N, d, 0.125, causal, NULL)
+
+    assert call(causal=2) == FA_ERR_ARG
+    assert call(d=96) == FA_ERR_HEADDIM
+    assert call(N=-1) == FA_ERR_SHAPE
+    for i in range(9):
+        ptrs = [P] * 9
+        ptrs[i] = NULL
+        assert call(ptrs=ptrs) == FA_ERR_NULL
+        ptrs[i] = PM
+        assert call(ptrs=ptrs) == FA_ERR_ALIGN
+    assert call(N=0, ptrs=[NULL] * 9) == FA_OK
+    assert call(B=1, H=1, N=(2 << 20) + 1) == FA_ERR_SCRATCH
+    assert call(B=64, H=32, N=1025) == FA_ERR_SCRATCH
+    assert call(B=3, H=5, N=(2 << 20) // 15 + 1, d=128) == FA_ERR_SCRATCH
+    assert "scratch" in fa.fa_strerror(FA_ERR_SCRATCH)
 
 
 def test_window_validation(lib):
