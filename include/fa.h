@@ -307,8 +307,16 @@ int fa_backward_grads_block_sparse(const void* q, const void* k, const void* v,
  *     (1 for an all-zero set), and the codes are e4m3(x / scale).
  *   - S_ij = scale * a_i b_t(j) (q8_i . k8_j) / d (without the / d when not
  *     rotated); the mask and lse follow S exactly as in fa_forward.
- *   - O_i = sum_j e4m3(P_ij) s v8_jc / sum_j P_ij with P_ij = exp(S_ij - max_j S_ij);
- *     the row sum uses the unrounded P.
+ *   - O_i = sum_j P~_ij s_{g(j),c} v8_jc / sum_j P_ij with the probabilities
+ *     taken relative to the row maximum rounded up to a whole power of two,
+ *     P_ij = 2^(log2(e) S_ij - m_i), m_i = ceil(log2(e) max_j S_ij), so
+ *     P_ij lies in (0, 1], and rounded with the power-of-two scale 2^-8:
+ *     P~_ij = 2^-8 e4m3(2^8 P_ij) (the tile-by-tile kernel rounds P against
+ *     its running reference, which may sit up to 2^2 above m_i and then
+ *     differs from this only below P = 2^-12, by at most 2^-16); the row sum
+ *     uses the unrounded P. These quantisation choices (scale sets, the
+ *     power-of-two reference, the 2^-8 scale) are this library's design, not
+ *     something the pages specify.
  * Arithmetic: Q~ and K~ in fp32 (butterflies), both products on the fp8
  * MFMA with fp32 accumulation, softmax in fp32; o is bf16 (nearest even),
  * lse fp32. Inputs must be finite (a NaN or infinity is not propagated).

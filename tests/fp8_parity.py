@@ -1,4 +1,8 @@
-"""Parity check of the FP8 forward against the oracle (oracle.forward_fp8_head).
+"""Check of the FP8 kernel against its own quantisation design
+(oracle.forward_fp8_head follows that design: per-row Q scales, 64-key-tile
+K scales, 32-key V blocks, P relative to a power-of-two reference and
+rounded with the scale 2^-8). This is not the parity of record, which is
+the kernel-independent bound against exact attention in fp8_exact_bound.py.
 
 Both sides round the same values onto the same e4m3 grids, so their results
 are identical except where a value lies so close to a rounding midpoint that
