@@ -4,14 +4,18 @@ A step is one pass of the whole hot path over one batch: fa_forward, then
 fa_backward_prep and fa_backward_grads, on the causal workload B=4, H=16,
 N=4096, d=128 (bf16 inputs drawn i.i.d. N(0,1) from seed 5, already resident
 in HBM). The timed region is exactly --steps steps, bracketed by device
-synchronisation; HIP events on the launch stream also time each of the three
-launches of every step.
+synchronisation and two HIP events on the launch stream.
 
 Throughput counts matmul FLOPs only: forward 4*B*H*N^2*d, backward 2.5x that
 (score recompute, dV, dP, dQ, dK), both halved under the causal mask.
 
-Prints one JSON line. `value` is forward+backward TFLOP/s; `fwd_tflops` the
-forward alone on the same input. `roofline` describes the dominant kernel
+Prints one JSON line. `value` is forward+backward TFLOP/s over the timed
+steps, which hold nothing but the steps' launches; `fwd_tflops` the forward
+alone on the same input. The duration of each launch kind (`ms`, and the
+roofline's `avg_launch_ms`) is the mean of --steps launches of that kind
+alone, back to back between two HIP events on the launch stream, right after
+the timed steps: an event around every single launch would add the event's
+own latency (about 10-15 us) to every launch. `roofline` describes the dominant kernel
 (the one with the longest launches), `cpu_baseline` the fp64 CPU oracle
 timed on a bounded sample of the same workload on this host.
 
@@ -39,10 +43,23 @@ N=4096, d=128 (seed 9) with a block-sparse mask per query head (each
 blocks always) through the _block_sparse calls; its FLOP count is 4*d per
 visible (query, key) pair, counted exactly from the mask.
 
+A seventh, `fwd_configs`, times the forward alone (fa_forward) on the three
+forward workloads: B=8, H=16, N=2048, d=64, no mask (seed 2); B=4, H=32,
+N=4096, d=128, causal (seed 3); B=1, H=16, N=32768, d=128, causal (seed 4),
+each with its own roofline.
+
+Besides the back-to-back timing (the mean of --steps launches between two
+HIP events, after --warmup untimed ones), every launch kind is also
+timed --flush-iters times with the L2 and the 256 MB MALL flushed before
+each launch (a 512 MiB write, not timed), reported as median and minimum
+(`flushed`): the launches then read their inputs from HBM, as the first
+kernel touching a tensor does.
+
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--no-cpu-baseline]
                        [--copy-calibration] [--no-gqa] [--gqa-only] [--no-window]
                        [--window-only] [--no-fp8] [--fp8-only] [--no-d256] [--d256-only]
-                       [--no-block-sparse] [--block-sparse-only]
+                       [--no-block-sparse] [--block-sparse-only] [--no-fwd-configs]
+                       [--fwd-configs-only] [--flush-iters 20]
 The default warm-up (100 steps, about 0.13 s on the main workload) brings
 the GPU to its steady clock first: with 5 warm-up steps the same 50 timed
 steps read about 2% lower, and longer warm-ups (500, 2000) no higher.
@@ -74,6 +91,7 @@ WORKLOAD = "fwdbwd_causal_b4h16n4096d128"
 GQA_WORKLOAD = "fwdbwd_causal_gqa_b4h32kv8n4096d128"
 WINDOW_WORKLOAD = "fwdbwd_window1024_b4h16n4096d128"
 BLOCK_SPARSE_WORKLOAD = "fwdbwd_causal_blocksparse50_b4h16n4096d128"
+FWD_WORKLOADS = ["fwd_b8h16n2048d64", "fwd_causal_b4h32n4096d128", "fwd_causal_b1h16n32768d128"]
 METRIC = "attention TFLOP/s (fwd, fwd+bwd) bf16 on 1 MI355X; % of MFMA peak"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["exact_io_aware_14_amd/csrc/fa_common.h", "exact_io_aware_14_amd/csrc/fa_fwd_kernel.h",
@@ -173,19 +191,43 @@ def cpu_baseline(w, heads: int):
                       f"in fp64 numpy, {dt:.1f} s; the rate extrapolates linearly to all heads"}
 
 
-def time_steps(step, steps, warmup, stream):
-    """Run `step(ev)` warmup + steps times; returns the mean ms of each of the
-    three launches of a step (HIP events on `stream`) and of the whole step."""
+def time_launches(launches, reps, stream):
+    """Average ms of each callable in `launches`, each launched `reps` times
+    back to back between two HIP events on `stream` (after one untimed
+    launch). The launches are idempotent: they read inputs the step leaves in
+    place and rewrite the same outputs."""
+    import torch
+    out = []
+    for fn in launches:
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / reps)
+    return out
+
+
+def time_steps(step, launches, steps, warmup, stream):
+    """`warmup` untimed steps, then `steps` steps between two HIP events (no
+    event inside, so nothing but the step's own launches is timed): the mean
+    ms per step. Then each launch kind of the step alone, back to back
+    (time_launches): its mean ms per launch."""
     import torch
     for _ in range(warmup):
-        step(None)
+        step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    for i in range(steps):
-        step(events[i])
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
     torch.cuda.synchronize()
-    parts = [sum(e[j].elapsed_time(e[j + 1]) for e in events) / steps for j in range(3)]
-    return parts, sum(e[0].elapsed_time(e[3]) for e in events) / steps
+    return time_launches(launches, steps, stream), e0.elapsed_time(e1) / steps
 
 
 def measure_variant(name, steps, warmup):
@@ -210,20 +252,18 @@ def measure_variant(name, steps, warmup):
     win = (w.window_left, w.window_right)
     causal_win = (-1, 0) if w.causal else (-1, -1)
 
-    def step(ev):
-        if ev is not None:
-            ev[0].record(stream)
+    def fwd():
         if sparse:
             fa.fa_forward_block_sparse(q, k, v, bm, *causal_win, w.scale, o, lse, stream=stream)
         elif window:
             fa.fa_forward_window(q, k, v, *win, w.scale, o, lse, stream=stream)
         else:
             fa.fa_forward_gqa(q, k, v, w.scale, w.causal, o, lse, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def prep():
         fa.fa_backward_prep(o, do, lse, ws, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def grads():
         if sparse:
             fa.fa_backward_grads_block_sparse(q, k, v, do, lse, ws, bm, *causal_win, w.scale, dq,
                                               dk, dv, stream=stream)
@@ -233,10 +273,14 @@ def measure_variant(name, steps, warmup):
         else:
             fa.fa_backward_grads_gqa(q, k, v, do, lse, ws, w.scale, w.causal, dq, dk, dv,
                                      stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
 
-    (fwd_ms, prep_ms, grads_ms), step_ms = time_steps(step, steps, warmup, stream)
+    def step():
+        fwd()
+        prep()
+        grads()
+
+    (fwd_ms, prep_ms, grads_ms), step_ms = time_steps(step, [fwd, prep, grads], steps, warmup,
+                                                      stream)
     fwd_f, bwd_f = counted_flops(w)
     out = {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d}
     if window:
@@ -257,7 +301,7 @@ def measure_variant(name, steps, warmup):
 
 def measure_fp8(steps, warmup):
     """The FP8 forward (prepare + attention) and the bf16 forward on the same
-    causal input; HIP events time each launch."""
+    causal input; each launch kind timed back to back between HIP events."""
     import torch
 
     import exact_io_aware_14_amd as fa
@@ -273,20 +317,22 @@ def measure_fp8(steps, warmup):
     lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev):
-        if ev is not None:
-            ev[0].record(stream)
+    def prepare():
         fa.fa_fp8_prepare(q, k, v, signs, ws, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        fa.fa_forward_fp8_prepared(ws, shape, w.scale, w.causal, o, lse, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        fa.fa_forward(q, k, v, w.scale, w.causal, o, lse, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
 
-    (prep_ms, attn_ms, bf16_ms), _ = time_steps(step, steps, warmup, stream)
+    def attention():
+        fa.fa_forward_fp8_prepared(ws, shape, w.scale, w.causal, o, lse, stream=stream)
+
+    def bf16():
+        fa.fa_forward(q, k, v, w.scale, w.causal, o, lse, stream=stream)
+
+    def step():
+        prepare()
+        attention()
+        bf16()
+
+    (prep_ms, attn_ms, bf16_ms), _ = time_steps(step, [prepare, attention, bf16], steps, warmup,
+                                                stream)
     fwd_f, _ = counted_flops(w)
     attn = fwd_f / (attn_ms * 1e-3) / 1e12
     return {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
@@ -303,6 +349,82 @@ def measure_fp8(steps, warmup):
                          "traffic": measured_traffic("fwd_fp8_kernel<128,causal>",
                                                      kernel_source_hash(), FP8_WORKLOAD),
                          "avg_launch_ms": round(attn_ms, 4)}}
+
+
+_FLUSH = None
+
+
+def flush_caches():
+    """Write 512 MiB (twice the 256 MB MALL, far above the L2s) so that the
+    next launch finds none of its inputs in any cache."""
+    import torch
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
+    _FLUSH.zero_()
+
+
+def time_flushed(launches, iters, stream):
+    """Each callable in `launches` timed `iters` times with HIP events around
+    it, the caches flushed before each launch: {index: (median_ms, min_ms)}.
+    The launches run in order within an iteration, so each one reads what
+    the previous one wrote."""
+    import statistics
+
+    import torch
+    times = [[] for _ in launches]
+    for _ in range(iters):
+        for j, fn in enumerate(launches):
+            flush_caches()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[j].append(e0.elapsed_time(e1))
+    return [(statistics.median(t), min(t)) for t in times]
+
+
+def measure_forward(name, steps, warmup, flush_iters):
+    """fa_forward alone on a forward workload: the mean of `steps`
+    back-to-back launches (between two HIP events) and the flushed median."""
+    import torch
+
+    import exact_io_aware_14_amd as fa
+    from exact_io_aware_14_amd.inputs import by_name, draw
+
+    w = by_name(name)
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in draw(w.shape, w.seed))
+    o = torch.empty_like(q)
+    lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        fa.fa_forward(q, k, v, w.scale, w.causal, o, lse, stream=stream)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ms, = time_launches([launch], steps, stream)
+    (fl_med, fl_min), = time_flushed([launch], flush_iters, stream) if flush_iters else [(None, None)]
+    fwd_f, _ = counted_flops(w)
+    tflops = fwd_f / (ms * 1e-3) / 1e12
+    kname = f"fwd_kernel<{w.d},{'causal' if w.causal else 'nomask'}>"
+    out = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+           "steps": steps, "ms": round(ms, 4), "fwd_tflops": round(tflops, 2),
+           "fwd_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    if fl_med is not None:
+        out["flushed"] = {"iters": flush_iters, "median_ms": round(fl_med, 4),
+                          "min_ms": round(fl_min, 4),
+                          "fwd_tflops_median": round(fwd_f / (fl_med * 1e-3) / 1e12, 2)}
+    out["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": round(tflops, 2),
+                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                       "traffic": measured_traffic(kname, kernel_source_hash(), w.name),
+                       "avg_launch_ms": round(ms, 4)}
+    return out
 
 
 def copy_calibration():
@@ -336,6 +458,11 @@ def main():
     ap.add_argument("--no-block-sparse", action="store_true")
     ap.add_argument("--block-sparse-only", action="store_true",
                     help="time only the block-sparse step (for its profile)")
+    ap.add_argument("--no-fwd-configs", action="store_true")
+    ap.add_argument("--fwd-configs-only", action="store_true",
+                    help="time only the forward workloads (for their profiles)")
+    ap.add_argument("--flush-iters", type=int, default=20,
+                    help="flushed-cache timings per launch kind (0: none)")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--fp8-only", action="store_true",
                     help="time only the FP8 forward (for its profile)")
@@ -354,6 +481,11 @@ def main():
     if args.d256_only:
         print(json.dumps({"d256": measure_variant(D256_WORKLOAD, args.steps, args.warmup)}),
               flush=True)
+        return
+    if args.fwd_configs_only:
+        print(json.dumps({"fwd_configs": {n: measure_forward(n, args.steps, args.warmup,
+                                                             args.flush_iters)
+                                          for n in FWD_WORKLOADS}}), flush=True)
         return
     if args.fp8_only:
         print(json.dumps({"fp8": measure_fp8(args.steps, args.warmup)}), flush=True)
@@ -382,44 +514,61 @@ def main():
     ws = torch.empty(fa_backward_workspace_size(*w.shape), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def fwd():
         fa_forward(q, k, v, w.scale, w.causal, o, lse, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def prep():
         fa_backward_prep(o, do, lse, ws, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def grads():
         fa_backward_grads(q, k, v, do, lse, ws, w.scale, w.causal, dq, dk, dv, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
+
+    def step():
+        fwd()
+        prep()
+        grads()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # the timed region: exactly --steps steps, nothing else inside
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    prep_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    grads_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    # each launch kind alone, --steps launches back to back (time_launches)
+    fwd_ms, prep_ms, grads_ms = time_launches([fwd, prep, grads], args.steps, stream)
     fwd_f, bwd_f = counted_flops(w)
     value = (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
     fwd_tflops = fwd_f / (fwd_ms * 1e-3) / 1e12
     bwd_tflops = bwd_f / ((prep_ms + grads_ms) * 1e-3) / 1e12
+
+    flushed = None
+    if args.flush_iters:
+        parts = time_flushed(
+            [lambda: fa_forward(q, k, v, w.scale, w.causal, o, lse, stream=stream),
+             lambda: fa_backward_prep(o, do, lse, ws, stream=stream),
+             lambda: fa_backward_grads(q, k, v, do, lse, ws, w.scale, w.causal, dq, dk, dv,
+                                       stream=stream)], args.flush_iters, stream)
+        (f_med, f_min), (p_med, p_min), (g_med, g_min) = parts
+        flushed = {"iters": args.flush_iters,
+                   "median_ms": {"fwd": round(f_med, 4), "bwd_prep": round(p_med, 4),
+                                 "bwd_grads": round(g_med, 4)},
+                   "min_ms": {"fwd": round(f_min, 4), "bwd_prep": round(p_min, 4),
+                              "bwd_grads": round(g_min, 4)},
+                   "fwdbwd_tflops_median": round((fwd_f + bwd_f) /
+                                                 ((f_med + p_med + g_med) * 1e-3) / 1e12, 2),
+                   "fwd_tflops_median": round(fwd_f / (f_med * 1e-3) / 1e12, 2)}
 
     src_hash = kernel_source_hash()
     if grads_ms >= fwd_ms:
@@ -458,6 +607,8 @@ def main():
         "kernel_source_hash": src_hash,
         "roofline": roofline,
     }
+    if flushed is not None:
+        out["flushed"] = flushed
     if not args.no_gqa:
         out["gqa"] = measure_variant(GQA_WORKLOAD, args.steps, args.warmup)
     if not args.no_window:
@@ -468,6 +619,9 @@ def main():
         out["block_sparse"] = measure_variant(BLOCK_SPARSE_WORKLOAD, args.steps, args.warmup)
     if not args.no_fp8:
         out["fp8"] = measure_fp8(args.steps, args.warmup)
+    if not args.no_fwd_configs:
+        out["fwd_configs"] = {n: measure_forward(n, args.steps, args.warmup, args.flush_iters)
+                              for n in FWD_WORKLOADS}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
     print(json.dumps(out), flush=True)
