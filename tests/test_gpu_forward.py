@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from exact_io_aware_14_amd import fa_forward, fa_forward_f32
+from exact_io_aware_14_amd import fa_forward, fa_forward_block_sparse, fa_forward_f32
 from exact_io_aware_14_amd.inputs import WORKLOADS, draw, to_f64
 from parity import check_lse, check_o, check_o_peaked, log, sample_heads, sample_rows
 
@@ -110,6 +110,34 @@ def test_forward_large_offset():
                                  1.0 / math.sqrt(d), True)
     check_o_peaked(o.float().cpu().numpy()[0, 0], ro, np.max(np.abs(to_f64(v))), "offset")
     check_lse(lse.cpu().numpy()[0, 0], rl, "offset")
+
+
+@pytest.mark.parametrize("N", [1, 64, 100, 128, 129, 150, 200, 333, 640, 1000, 8192, 8320])
+def test_forward_causal_block_pairs(N):
+    """Causal d = 128 launches up to 64 query blocks per head (N <= 8192) give
+    each workgroup blocks nqb-1-i and i: odd block counts leave the middle
+    block alone, a ragged last block can end on an odd tile count (no tile
+    prefetched across the two blocks). Against the oracle (sampled rows at the
+    largest lengths), and bitwise against the block-sparse kernel with an
+    all-ones mask, which computes every row alike without pairing."""
+    B, H, d = 1, 2, 128
+    q, k, v = draw((B, H, N, d), 4000 + N)
+    log(f"case causal pairs N={N}")
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    o, lse = fa_forward(qd, kd, vd, causal=True)
+    nb = (N + 127) // 128
+    ones = torch.ones((nb, nb), dtype=torch.uint8, device=DEV)
+    o2, l2 = fa_forward_block_sparse(qd, kd, vd, ones, -1, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    rows = sample_rows(N, seed=N) if N > 2000 else None
+    for h in range(H):
+        ro, rl = oracle.forward_head(to_f64(q[0, h]), to_f64(k[0, h]), to_f64(v[0, h]),
+                                     d ** -0.5, True, rows=rows)
+        got_o, got_l = (o[0, h], lse[0, h]) if rows is None else (o[0, h][rows], lse[0, h][rows])
+        check_o(got_o, ro, f"N={N} h={h}")
+        check_lse(got_l, rl, f"N={N} h={h}")
 
 
 def test_forward_f32_workload():
