@@ -148,6 +148,16 @@ def counted_flops(w):
     return fwd, 2.5 * fwd
 
 
+def fwd_kernel_name(w):
+    """The forward kernel fa_forward launches on workload w, as the profiles
+    name it: causal launches at d = 128 with at most 64 query blocks per head
+    take two query blocks per workgroup (`pair`)."""
+    if not w.causal:
+        return f"fwd_kernel<{w.d},nomask>"
+    pair = w.d == 128 and (w.N + 127) // 128 <= 64
+    return f"fwd_kernel<{w.d},causal{',pair' if pair else ''}>"
+
+
 def measured_traffic(kernel: str, src_hash: str, workload: str = WORKLOAD):
     """HBM bytes per launch of `kernel` on `workload` from the committed
     counter runs, if they were taken on the kernel sources as they are now;
@@ -411,7 +421,7 @@ def measure_forward(name, steps, warmup, flush_iters):
     (fl_med, fl_min), = time_flushed([launch], flush_iters, stream) if flush_iters else [(None, None)]
     fwd_f, _ = counted_flops(w)
     tflops = fwd_f / (ms * 1e-3) / 1e12
-    kname = f"fwd_kernel<{w.d},{'causal' if w.causal else 'nomask'}>"
+    kname = fwd_kernel_name(w)
     out = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
            "steps": steps, "ms": round(ms, 4), "fwd_tflops": round(tflops, 2),
            "fwd_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
@@ -574,7 +584,7 @@ def main():
     if grads_ms >= fwd_ms:
         kname, kflops, kms = "bwd_grads_kernel<128,causal>", bwd_f, grads_ms
     else:
-        kname, kflops, kms = "fwd_kernel<128,causal>", fwd_f, fwd_ms
+        kname, kflops, kms = fwd_kernel_name(w), fwd_f, fwd_ms
     achieved = kflops / (kms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
