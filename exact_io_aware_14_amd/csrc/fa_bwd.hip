@@ -160,8 +160,11 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   // its query heads are bh*group .. bh*group+group-1
   const size_t qhead0 = (size_t)bh * p.group * N;
 
-  const int k0 = kblk * kKeyBlock;
-  const int kw0 = k0 + 32 * kw;  // this wave's first key
+  // the job's keys, this wave's keys and the query tiles they walk
+  const sched::DkdvRange rng =
+      sched::dkdv_range<kKeyBlock, kTile>(kblk, kw, qh, N, p.wl, p.wr, CAUSAL);
+  const int k0 = rng.k0;
+  const int kw0 = rng.kw0;  // this wave's first key
   const int mykey = kw0 + col;
 
   Offsets<D> off;
@@ -202,9 +205,8 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   // Masked kernels (CAUSAL: a causal or local window): query row i sees key
   // j iff j - wr <= i <= j + wl, so the block's keys k0 .. kend are seen by
   // the rows of query tiles t0 .. ntiles-1 only.
-  const int kend = min(k0 + kKeyBlock, N) - 1;
-  const int t0 = CAUSAL ? max(0, k0 - p.wr) / kTile : 0;
-  const int ntiles = CAUSAL ? min(N - 1, kend + p.wl) / kTile + 1 : (N + kTile - 1) / kTile;
+  const int t0 = rng.t0;
+  const int ntiles = rng.ntiles;
   // rows that see this lane's key: lo_row .. lo_row + n_rows - 1, i.e.
   // j - wr .. j + wl (the count in unsigned: both bounds may be 2^30)
   const int lo_row = mykey - p.wr;
@@ -328,15 +330,8 @@ __device__ __forceinline__ void dkdv_job(const BwdParams& p, int bh, int kblk,
   // (masked), or show the wave none of its keys (skipped). Each wave walks
   // them in three loops (every iteration passes one barrier), so no loop
   // holds both versions of the tile body. Causal: no tiles after tm2.
-  int tm1 = t0, tm2 = ntiles;
-  if (CAUSAL) {
-    tm1 = min(ntiles, max(t0, ceil_div(kw0 + 31 - p.wr - 32 * qh, kTile)));
-    tm2 = min(ntiles, max(tm1, floor_div(kw0 + p.wl - 32 * qh - 31, kTile) + 1));
-  }
-  auto visible = [&](int t) {
-    const int r0 = t * kTile + 32 * qh;
-    return r0 + 31 >= kw0 - p.wr && r0 <= kw0 + 31 + p.wl;
-  };
+  const int tm1 = rng.tm1, tm2 = rng.tm2;
+  auto visible = [&](int t) { return sched::dkdv_visible<kTile>(t, rng, qh, p.wl, p.wr); };
   if constexpr (!SPARSE) {
     if (t0 < ntiles) fill(0, t0, 0);
     for (int jq = 0; jq < p.group; ++jq) {
@@ -454,10 +449,11 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   const uint16_t* kg = p.k + kvhead * D;
   const uint16_t* vg = p.v + kvhead * D;
 
-  const int q0 = qblk * kQBlock;
-  const int qw0 = q0 + wave * 32;
+  // the job's rows, this wave's rows and the key tiles they walk
+  const sched::DqRange rng = sched::dq_range<kQBlock, kTile>(qblk, wave, N, p.wl, p.wr, CAUSAL);
+  const int q0 = rng.q0;
+  const int qw0 = rng.qw0;
   const int myq = qw0 + col;
-  const int wave_last = min(qw0 + 32, N) - 1;
 
   Offsets<D> off;
   off.init(wave, lane);
@@ -486,12 +482,10 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   // Masked kernels (CAUSAL: a causal or local window): row i sees keys
   // i-wl .. i+wr. The workgroup walks key tiles kt0 .. ntiles-1, those that
   // one of its rows sees; this wave computes on tiles wt0 .. wt1-1.
-  const int ntiles_all = (N + kTile - 1) / kTile;
-  const int qend = min(q0 + kQBlock, N) - 1;
-  const int kt0 = CAUSAL ? max(0, q0 - p.wl) / kTile : 0;
-  const int ntiles = CAUSAL ? min(N - 1, qend + p.wr) / kTile + 1 : ntiles_all;
-  const int wt0 = CAUSAL ? max(0, qw0 - p.wl) / kTile : 0;
-  const int wt1 = qw0 >= N ? wt0 : (CAUSAL ? min(N - 1, wave_last + p.wr) / kTile + 1 : ntiles_all);
+  const int kt0 = rng.kt0;
+  const int ntiles = rng.ntiles;
+  const int wt0 = rng.wt0;
+  const int wt1 = rng.wt1;
   // keys this lane's row sees: lo_key .. lo_key + n_keys - 1, i.e. i - wl .. i + wr
   const int lo_key = myq - p.wl;
   const uint32_t n_keys = (uint32_t)p.wl + (uint32_t)p.wr + 1u;
@@ -579,13 +573,8 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
   // tm1 .. tm2-1 (t*64 >= wave_last-wl and t*64+63 <= qw0+wr); the visible
   // tiles before and after cross a window edge (masked). Three loops (every
   // iteration passes one barrier), so no loop holds both tile bodies.
-  // Causal: no masked tiles before tm1 = kt0 = 0.
-  int tm1 = kt0, tm2 = wt1;
-  if (CAUSAL) {
-    tm1 = min(ntiles, max(kt0, ceil_div(wave_last - p.wl, kTile)));
-    tm2 = min(wt1, max(tm1, floor_div(qw0 + p.wr - (kTile - 1), kTile) + 1));
-  }
-  if (qw0 >= N) tm2 = tm1;  // no rows: every tile is skipped
+  // Causal: no masked tiles before tm1 = kt0 = 0. No rows: tm2 = tm1.
+  const int tm1 = rng.tm1, tm2 = rng.tm2;
   auto visible = [&](int t) { return t >= wt0 && t < wt1; };
   if constexpr (!SPARSE) {
     fill(kt0);

@@ -7,6 +7,7 @@
 
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_schedule.h"
 
 namespace fa {
 namespace {
@@ -48,60 +49,14 @@ constexpr int kQBlockW = 128;    // query rows per dQ job
 
 // ---------------------------------------------------------------- layout
 
-// Job of this workgroup in the grads launch. Every K/V head owns nkb dK/dV
-// jobs and group * nqb dQ jobs (those of its query heads). The two kinds
-// are interleaved evenly, each sequence ordered from the most expensive
-// block down (causal: dK/dV of the first key blocks, dQ of the last query
-// blocks). Consecutive workgroups go to the 8 XCDs in turn;
-// when the head count allows, each XCD gets whole K/V heads (with their
-// query heads) so that their K/V and Q/dO stay in its L2.
-struct Job {
-  int bh;    // dK/dV: the K/V head (batch * K/V heads); dQ: the query head
-  int blk;
-  bool is_dq;
-};
+// Job of this workgroup in the grads launch (sched::grads_job in
+// fa_schedule.h: dK/dV and dQ jobs interleaved evenly over each K/V head's
+// slots, XCD-aware, the most expensive blocks first).
+using Job = sched::Job;
 
 template <bool CAUSAL>
 __device__ __forceinline__ Job job_of(const BwdParams& p) {
-  const int L = blockIdx.x;
-  const int ndq = p.group * p.nqb;
-  const int per_head = p.nkb + ndq;
-  const int bhkv = p.BH / p.group;
-  int kvh, j;
-  if (p.xcd_remap) {
-    const int xcd = L & 7, idx = L >> 3;
-    kvh = (idx / per_head) * 8 + xcd;
-    j = idx % per_head;
-  } else {
-    kvh = L % bhkv;
-    j = L / bhkv;
-  }
-  // The head's dQ jobs are spread evenly over its slots (slot j is a dQ job
-  // iff floor((j+1) ndq / per_head) > floor(j ndq / per_head)). Within an
-  // XCD, consecutive workgroups go to its four shader engines in turn, so
-  // each engine must see the same mix of the two kinds: where one engine
-  // gets only dK/dV jobs, workgroups wait for it while the other engines
-  // have free CUs. The even spread alone alternates the kinds when there
-  // are as many of each (at d = 256), which again splits them by engine;
-  // rotating the slots of each full group of four by the group index gives
-  // every engine both kinds in any case.
-  if ((j | 3) < per_head) j = (j & ~3) | (((j & 3) + (j >> 2)) & 3);
-  Job job;
-  const int before = (int)(((long long)j * ndq) / per_head);
-  const int after = (int)(((long long)(j + 1) * ndq) / per_head);
-  job.is_dq = after > before;
-  const int rank = job.is_dq ? before : j - before;
-  if (job.is_dq) {
-    // rank r: query block r / group (from the last one under the causal
-    // mask) of query head r % group of this K/V head
-    const int qbr = rank / p.group;
-    job.bh = kvh * p.group + rank % p.group;
-    job.blk = CAUSAL ? (p.nqb - 1 - qbr) : qbr;
-  } else {
-    job.bh = kvh;
-    job.blk = rank;
-  }
-  return job;
+  return sched::grads_job(blockIdx.x, p.BH, p.group, p.nkb, p.nqb, p.xcd_remap != 0, CAUSAL);
 }
 
 // Start loading 64 floats v[row0 .. row0+63] (zeros past N) into `dst`.

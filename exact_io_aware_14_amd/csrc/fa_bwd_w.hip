@@ -99,8 +99,12 @@ __device__ __forceinline__ void dkdv_job_w(const BwdParams& p, int bh, int kblk,
   const size_t head = (size_t)bh * N;  // bh: the K/V head
   const size_t qhead0 = (size_t)bh * p.group * N;
 
-  const int k0 = kblk * kKeyBlockW;
-  const int kw0 = k0 + 32 * wave;  // this wave's first key
+  // the job's keys, this wave's keys (all rows of each 32-row query tile)
+  // and the query tiles they walk
+  const sched::DkdvRange rng =
+      sched::dkdv_range<kKeyBlockW, kQTileW>(kblk, wave, 0, N, p.wl, p.wr, CAUSAL);
+  const int k0 = rng.k0;
+  const int kw0 = rng.kw0;  // this wave's first key
   const int mykey = kw0 + col;
 
   OffsetsW<D> off;
@@ -133,9 +137,8 @@ __device__ __forceinline__ void dkdv_job_w(const BwdParams& p, int bh, int kblk,
   }
 
   // masked kernels: the block's keys are seen by rows k0 - wr .. kend + wl
-  const int kend = min(k0 + kKeyBlockW, N) - 1;
-  const int t0 = CAUSAL ? max(0, k0 - p.wr) / kQTileW : 0;
-  const int ntiles = CAUSAL ? min(N - 1, kend + p.wl) / kQTileW + 1 : (N + kQTileW - 1) / kQTileW;
+  const int t0 = rng.t0;
+  const int ntiles = rng.ntiles;
   // rows that see this lane's key: lo_row .. lo_row + n_rows - 1, i.e.
   // j - wr .. j + wl (the count in unsigned: both bounds may be 2^30)
   const int lo_row = mykey - p.wr;
@@ -240,15 +243,8 @@ __device__ __forceinline__ void dkdv_job_w(const BwdParams& p, int bh, int kblk,
   // this wave's keys kw0 .. kw0+31 and the rows r0 .. r0+31 of tile t all
   // see each other for tiles tm1 .. tm2-1; the visible tiles before and
   // after are masked (three loops, every iteration passes one barrier)
-  int tm1 = t0, tm2 = ntiles;
-  if (CAUSAL) {
-    tm1 = min(ntiles, max(t0, ceil_div(kw0 + 31 - p.wr, kQTileW)));
-    tm2 = min(ntiles, max(tm1, floor_div(kw0 + p.wl - 31, kQTileW) + 1));
-  }
-  auto visible = [&](int t) {
-    const int r0 = t * kQTileW;
-    return r0 + 31 >= kw0 - p.wr && r0 <= kw0 + 31 + p.wl;
-  };
+  const int tm1 = rng.tm1, tm2 = rng.tm2;
+  auto visible = [&](int t) { return sched::dkdv_visible<kQTileW>(t, rng, 0, p.wl, p.wr); };
   if constexpr (!SPARSE) {
     if (t0 < ntiles) fill(0, t0, 0);
     for (int jq = 0; jq < p.group; ++jq) {
@@ -339,10 +335,13 @@ __device__ __forceinline__ void dq_job_w(const BwdParams& p, int bh, int qblk,
   const uint16_t* kg = p.k + kvhead * D;
   const uint16_t* vg = p.v + kvhead * D;
 
-  const int q0 = qblk * kQBlockW;
-  const int qw0 = q0 + wave * 32;
+  // the job's rows, this wave's rows and the key tiles they walk
+  const sched::DqRange rng =
+      sched::dq_range<kQBlockW, kKTileW>(qblk, wave, N, p.wl, p.wr, CAUSAL);
+  const int q0 = rng.q0;
+  const int qw0 = rng.qw0;
   const int myq = qw0 + col;
-  const int wave_last = min(qw0 + 32, N) - 1;
+  const int wave_last = rng.wave_last;
 
   OffsetsW<D> off;
   off.init(lane);
@@ -371,12 +370,10 @@ __device__ __forceinline__ void dq_job_w(const BwdParams& p, int bh, int qblk,
 #pragma unroll
   for (int i = 0; i < kDB; ++i) dqacc[i] = zero16();
 
-  const int ntiles_all = (N + kKTileW - 1) / kKTileW;
-  const int qend = min(q0 + kQBlockW, N) - 1;
-  const int kt0 = CAUSAL ? max(0, q0 - p.wl) / kKTileW : 0;
-  const int ntiles = CAUSAL ? min(N - 1, qend + p.wr) / kKTileW + 1 : ntiles_all;
-  const int wt0 = CAUSAL ? max(0, qw0 - p.wl) / kKTileW : 0;
-  const int wt1 = qw0 >= N ? wt0 : (CAUSAL ? min(N - 1, wave_last + p.wr) / kKTileW + 1 : ntiles_all);
+  const int kt0 = rng.kt0;
+  const int ntiles = rng.ntiles;
+  const int wt0 = rng.wt0;
+  const int wt1 = rng.wt1;
   // keys this lane's row sees: lo_key .. lo_key + n_keys - 1, i.e. i - wl .. i + wr
   const int lo_key = myq - p.wl;
   const uint32_t n_keys = (uint32_t)p.wl + (uint32_t)p.wr + 1u;
@@ -455,12 +452,7 @@ __device__ __forceinline__ void dq_job_w(const BwdParams& p, int bh, int qblk,
     __syncthreads();
     if (t + 1 < ntiles) fill(t + 1);
   };
-  int tm1 = kt0, tm2 = wt1;
-  if (CAUSAL) {
-    tm1 = min(ntiles, max(kt0, ceil_div(wave_last - p.wl, kKTileW)));
-    tm2 = min(wt1, max(tm1, floor_div(qw0 + p.wr - (kKTileW - 1), kKTileW) + 1));
-  }
-  if (qw0 >= N) tm2 = tm1;
+  const int tm1 = rng.tm1, tm2 = rng.tm2;
   auto visible = [&](int t) { return t >= wt0 && t < wt1; };
   if constexpr (!SPARSE) {
     fill(kt0);

@@ -39,6 +39,7 @@
 
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_schedule.h"
 
 namespace fa {
 namespace {
@@ -120,65 +121,35 @@ void fwd_kernel(FwdParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // ---- which (head, query block) this workgroup owns
-  int bh, qbr;
-  const int L = blockIdx.x;
-  // PAIR (causal mask): query blocks nqb-1-i and i of one head in turn, so
-  // every workgroup walks about nqb+1 key tiles (the middle block of an odd
-  // nqb alone); the second block's first key tile loads while the first
+  // ---- which (head, query block) this workgroup owns (fa_schedule.h):
+  // masked launches dispatch the longest rows first; PAIR launches (causal
+  // mask) take query blocks nqb-1-i and i of one head in turn, so every
+  // workgroup walks about nqb+1 key tiles (the middle block of an odd nqb
+  // alone), and the second block's first key tile loads while the first
   // block's last one is computed.
   static_assert(!PAIR || (CAUSAL && !SPARSE), "pairs are for the causal mask");
   constexpr bool pair = PAIR;
-  int npass = 1, qb_second = 0;
-  if (pair) {
-    const int npair = (p.nqb + 1) / 2;
-    int pi;
-    if (p.xcd_remap) {
-      const int xcd = L & 7, idx = L >> 3, slot = idx / npair;
-      bh = ((slot / p.group) * 8 + xcd) * p.group + slot % p.group;
-      pi = idx % npair;
-    } else {
-      bh = L % p.BH;
-      pi = L / p.BH;
-    }
-    qbr = pi;  // the first block is nqb-1-pi
-    qb_second = pi;
-    npass = (p.nqb - 1 - pi) != pi ? 2 : 1;
-  } else if (p.xcd_remap) {
-    // Consecutive workgroups go to the 8 XCDs in turn; each XCD gets whole
-    // K/V heads (with all query heads that read them) so the K/V of a head
-    // is re-read from that XCD's L2. Query head bh reads K/V head
-    // bh / group: the query heads of K/V head kv are kv*group .. +group-1.
-    // Within an XCD the heads go out in pairs under the causal mask, the
-    // blocks of a pair rank by rank (both heads' longest block, then the
-    // next), which balances the uneven block lengths while only about two
-    // heads' K/V are in flight; head by head without the mask, where all
-    // blocks are alike.
-    const int xcd = L & 7, idx = L >> 3, hx = p.BH >> 3;
-    const int g2 = (CAUSAL && hx % 2 == 0) ? 2 : 1;  // heads per group
-    const int grp = idx / (g2 * p.nqb), within = idx % (g2 * p.nqb);
-    const int slot = grp * g2 + within % g2;
-    bh = ((slot / p.group) * 8 + xcd) * p.group + slot % p.group;
-    qbr = within / g2;
-  } else {
-    bh = L % p.BH;
-    qbr = L / p.BH;
-  }
+  const sched::FwdBlock blk =
+      sched::fwd_block(blockIdx.x, p.BH, p.group, p.nqb, p.xcd_remap != 0, CAUSAL, PAIR);
+  const int bh = blk.bh;
+  const int npass = blk.npass;
   const int N = p.N;
   bool prefetched = false;  // this pass's first key tile is already loading into stage 0
   for (int pass = 0; pass < npass; ++pass) {
-  // causal: the longest rows (most key tiles) are dispatched first
-  const int qb = pass == 1 ? qb_second : (CAUSAL ? (p.nqb - 1 - qbr) : qbr);
+  const int qb = pass == 1 ? blk.qb_second : blk.qb_first;
   const size_t head_off = (size_t)bh * (size_t)N * D;
   const size_t kv_off = (size_t)(bh / p.group) * (size_t)N * D;
   const TIn* qg = reinterpret_cast<const TIn*>(p.q) + head_off;
   const TIn* kg = reinterpret_cast<const TIn*>(p.k) + kv_off;
   const TIn* vg = reinterpret_cast<const TIn*>(p.v) + kv_off;
 
-  const int q0 = qb * kBR;                                        // first row of the block
-  const int qw0 = q0 + wave * kRowsPerWave;                       // this wave's
-  const int myq = qw0 + col;                                      // this lane's row
-  const int wave_last = min(qw0 + kRowsPerWave, N) - 1;
+  // rows of the block and of this wave, and the key tiles they walk
+  const sched::FwdRange rng =
+      sched::fwd_range<kBR, kRowsPerWave, BC>(qb, wave, N, p.wl, p.wr, CAUSAL);
+  const int q0 = rng.q0;                // first row of the block
+  const int qw0 = rng.qw0;              // this wave's
+  const int myq = qw0 + col;            // this lane's row
+  const int wave_last = rng.wave_last;
   // keys this lane's row sees: lo_key .. lo_key + n_vis - 1 (masked kernels:
   // i - wl .. i + wr within 0 .. N-1; otherwise 0 .. N-1)
   const int lo_key = CAUSAL ? myq - p.wl : 0;
@@ -223,17 +194,14 @@ void fwd_kernel(FwdParams p) {
   f32x16 s[kKB];            // S^T of the tile between its MFMA and VALU phases
   uint32_t pk[kKB][8];      // P^T packed to bf16, between its VALU and MFMA phases
 
-  const int ktiles_all = (N + BC - 1) / BC;
-  // tiles the workgroup walks, and tiles with a visible key for this wave
   // Masked kernels (CAUSAL: a causal or local window, bounds wl, wr; an
   // unbounded side is 2^30): the workgroup walks key tiles t_first ..
   // t_end-1, those holding a key that one of its rows sees, and each wave
   // computes on the tiles [wt_first, wt_end) that hold one of its keys.
-  const int qlast = min(q0 + kBR, N) - 1;
-  const int t_first = CAUSAL ? max(0, q0 - p.wl) / BC : 0;
-  const int t_end = CAUSAL ? min(N - 1, qlast + p.wr) / BC + 1 : ktiles_all;
-  const int wt_first = CAUSAL ? max(0, qw0 - p.wl) / BC : 0;
-  const int wt_end = qw0 >= N ? wt_first : (CAUSAL ? min(N - 1, wave_last + p.wr) / BC + 1 : ktiles_all);
+  const int t_first = rng.t_first;
+  const int t_end = rng.t_end;
+  const int wt_first = rng.wt_first;
+  const int wt_end = rng.wt_end;
   const float c = p.c;
 
   // start loading key tile t of g (K or V) into the stage array dst
@@ -303,8 +271,7 @@ void fwd_kernel(FwdParams p) {
     const int key0 = t * BC;
     // a tile needs masks where it passes N, the first row's upper bound or
     // the last row's lower bound
-    const bool need_mask =
-        (key0 + BC > N) || (CAUSAL && (key0 + BC - 1 > qw0 + p.wr || key0 < wave_last - p.wl));
+    const bool need_mask = sched::fwd_need_mask<BC>(t, rng, N, p.wl, p.wr, CAUSAL);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
