@@ -170,8 +170,8 @@ __host__ __device__ inline Job grads_job(int L, int BH, int group, int nkb, int 
 }
 
 // dK/dV job of key block kblk (KB keys), wave (kw, qh): keys kw0 .. kw0+31
-// and rows 32 qh .. 32 qh + 31 of every query tile of T rows. The job walks
-// query tiles t0 .. ntiles-1 (those holding a row that sees one of its
+// and rows RW qh .. RW qh + RW-1 of every query tile of T rows. The job
+// walks query tiles t0 .. ntiles-1 (those holding a row that sees one of its
 // keys); the wave's rows see all of its keys in tiles tm1 .. tm2-1 (no
 // mask), and the tiles before and after cross a window edge or show the
 // wave none of its keys (dkdv_visible).
@@ -179,7 +179,7 @@ struct DkdvRange {
   int k0, kw0, kend, t0, ntiles, tm1, tm2;
 };
 
-template <int KB, int T>
+template <int KB, int T, int RW = 32>
 __host__ __device__ inline DkdvRange dkdv_range(int kblk, int kw, int qh, int N, int wl, int wr,
                                                 bool masked) {
   DkdvRange r;
@@ -191,16 +191,16 @@ __host__ __device__ inline DkdvRange dkdv_range(int kblk, int kw, int qh, int N,
   r.tm1 = r.t0;
   r.tm2 = r.ntiles;
   if (masked) {
-    r.tm1 = imin(r.ntiles, imax(r.t0, ceil_div(r.kw0 + 31 - wr - 32 * qh, T)));
-    r.tm2 = imin(r.ntiles, imax(r.tm1, floor_div(r.kw0 + wl - 32 * qh - 31, T) + 1));
+    r.tm1 = imin(r.ntiles, imax(r.t0, ceil_div(r.kw0 + 31 - wr - RW * qh, T)));
+    r.tm2 = imin(r.ntiles, imax(r.tm1, floor_div(r.kw0 + wl - RW * qh - (RW - 1), T) + 1));
   }
   return r;
 }
 
-template <int T>
+template <int T, int RW = 32>
 __host__ __device__ inline bool dkdv_visible(int t, const DkdvRange& r, int qh, int wl, int wr) {
-  const int r0 = t * T + 32 * qh;
-  return r0 + 31 >= r.kw0 - wr && r0 <= r.kw0 + 31 + wl;
+  const int r0 = t * T + RW * qh;
+  return r0 + (RW - 1) >= r.kw0 - wr && r0 <= r.kw0 + 31 + wl;
 }
 
 // dQ job of query block qblk (QB rows), wave `wave` (32 rows): the job walks

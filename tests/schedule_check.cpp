@@ -186,7 +186,8 @@ static void check_forward_ranges(int N, const Mask& m) {
 // ---------------------------------------------------------------- backward
 
 static void check_grads_map(int BH, int group, int N, bool masked, int KB, int QB) {
-  const int nkb = (N + KB - 1) / KB, nqb = (N + QB - 1) / QB;
+  // KB or QB 0: a launch of the other job kind only
+  const int nkb = KB ? (N + KB - 1) / KB : 0, nqb = QB ? (N + QB - 1) / QB : 0;
   const int bhkv = BH / group;
   const bool xcd = bhkv % 8 == 0;
   const long long grid = (long long)bhkv * (nkb + group * nqb);
@@ -213,7 +214,7 @@ static void check_grads_map(int BH, int group, int N, bool masked, int KB, int Q
 
 // dK/dV job: key blocks of KB keys, query tiles of T rows; a wave owns 32
 // keys (kw) and the 32 rows 32 qh .. of every tile.
-template <int KB, int T>
+template <int KB, int T, int RW = 32>
 static void check_dkdv(int N, const Mask& m, int n_kw, int n_qh) {
   const int nkb = (N + KB - 1) / KB;
   const int ntiles_all = (N + T - 1) / T;
@@ -221,17 +222,18 @@ static void check_dkdv(int N, const Mask& m, int n_kw, int n_qh) {
   for (int kblk = 0; kblk < nkb; ++kblk)
     for (int kw = 0; kw < n_kw; ++kw)
       for (int qh = 0; qh < n_qh; ++qh) {
-        const s::DkdvRange r = s::dkdv_range<KB, T>(kblk, kw, qh, N, m.wl, m.wr, m.masked);
+        const s::DkdvRange r = s::dkdv_range<KB, T, RW>(kblk, kw, qh, N, m.wl, m.wr, m.masked);
         CHECK(r.t0 >= 0 && r.ntiles <= ntiles_all && r.t0 <= r.tm1 && r.tm1 <= r.tm2 &&
                   r.tm2 <= r.ntiles,
               "dkdv range: %d %d %d %d of %d", r.t0, r.tm1, r.tm2, r.ntiles, ntiles_all);
         const int ka = r.kw0, kb = std::min(N, r.kw0 + 32) - 1;  // the wave's keys
         if (ka > kb) continue;
         for (int t = 0; t < ntiles_all; ++t) {
-          const int ra = t * T + 32 * qh, rb = std::min(N, ra + 32) - 1;  // the wave's rows of t
+          const int ra = t * T + RW * qh, rb = std::min(N, ra + RW) - 1;  // the wave's rows of t
           const bool walked = t >= r.t0 && t < r.ntiles;
           const bool unmasked = t >= r.tm1 && t < r.tm2;
-          const bool computed = unmasked || (walked && s::dkdv_visible<T>(t, r, qh, m.wl, m.wr));
+          const bool computed =
+              unmasked || (walked && s::dkdv_visible<T, RW>(t, r, qh, m.wl, m.wr));
           if (!computed)
             CHECK(none_visible(m, ra, rb, ka, kb, N, brute),
                   "dkdv: tile %d skipped with a visible pair (kblk %d kw %d qh %d N %d wl %d wr %d)",
@@ -309,6 +311,7 @@ int main() {
       check_forward_ranges(N, m);
       check_dkdv<128, 64>(N, m, 4, 2);  // d <= 128: 128-key jobs, 64-row tiles, 8 waves
       check_dkdv<128, 32>(N, m, 4, 1);  // d = 256: 128-key jobs, 32-row tiles, 4 waves
+      check_dkdv<128, 128, 128>(N, m, 4, 1);  // d = 128: 128-key jobs, 128-row tiles, 4 waves
       check_dq<256, 64>(N, m);          // d <= 128: 256-row jobs, 64-key tiles
       check_dq<128, 64>(N, m);          // d = 256: 128-row jobs, 64-key tiles
     }
@@ -320,6 +323,8 @@ int main() {
         if (masked) check_forward_map(g[0], g[1], N, true, true);
         check_grads_map(g[0], g[1], N, masked, 128, 256);
         check_grads_map(g[0], g[1], N, masked, 128, 128);
+        check_grads_map(g[0], g[1], N, masked, 128, 0);  // launches of one job kind
+        check_grads_map(g[0], g[1], N, masked, 0, 256);
       }
   }
   std::printf("%lld checks, %lld failures\n", g_checks, g_fail);
