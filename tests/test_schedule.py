@@ -80,11 +80,14 @@ MUTATIONS = [
      "job.bh = kvh * group + rank % group;",
      "job.bh = kvh + rank % group;"),
     ("dkdv_unmasked_one_tile_long",
-     "floor_div(r.kw0 + wl - 32 * qh - 31, T) + 1));",
-     "floor_div(r.kw0 + wl - 32 * qh - 31, T) + 2));"),
+     "floor_div(r.kw0 + wl - RW * qh - (RW - 1), T) + 1));",
+     "floor_div(r.kw0 + wl - RW * qh - (RW - 1), T) + 2));"),
     ("dkdv_visible_first_row_only",
-     "return r0 + 31 >= r.kw0 - wr && r0 <= r.kw0 + 31 + wl;",
+     "return r0 + (RW - 1) >= r.kw0 - wr && r0 <= r.kw0 + 31 + wl;",
      "return r0 >= r.kw0 - wr && r0 <= r.kw0 + 31 + wl;"),
+    ("dkdv_wave_rows_fixed_at_32",
+     "return r0 + (RW - 1) >= r.kw0 - wr && r0 <= r.kw0 + 31 + wl;",
+     "return r0 + 31 >= r.kw0 - wr && r0 <= r.kw0 + 31 + wl;"),
     ("dkdv_first_tile_from_wave_key",
      "r.t0 = masked ? imax(0, r.k0 - wr) / T : 0;",
      "r.t0 = masked ? imax(0, r.kw0 - wr) / T : 0;"),
