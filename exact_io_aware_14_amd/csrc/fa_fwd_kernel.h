@@ -74,10 +74,12 @@ struct FwdParams {
 
 // Workgroup shape: four waves (128 query rows), two workgroups per CU at
 // d = 128 (four at d = 64 with bf16 inputs, at most 128 VGPRs); the waves a SIMD holds belong
-// to different workgroups and overlap freely. At d = 256 one workgroup per
-// CU: its four LDS stages take 128 KB, and a wave's Q (64 registers) and O
-// accumulators (128) need the SIMD's whole register file (512, accumulators
-// in AGPRs).
+// to different workgroups and overlap freely. At d = 256 a wave's Q (64
+// registers) and O accumulators (128) leave room for the scores of 32 keys
+// only: bf16 inputs take 32-key tiles (two LDS stages of K and V, 64 KB) at
+// two workgroups per CU, 256 registers per wave; fp32 inputs and
+// block-sparse masks take 64-key tiles at one workgroup per CU (128 KB of
+// stages, the SIMD's whole register file of 512).
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
@@ -93,10 +95,10 @@ struct Layout {
 // PAIR: two query blocks per workgroup under the causal mask (see below).
 template <int D, int BC, bool CAUSAL, typename TIn, typename TOut, bool SPARSE = false,
           bool PAIR = false>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : (D == 64 && sizeof(TIn) == 2 ? 4 : 2))
+__global__ __launch_bounds__(kThreads, D == 256 ? (BC == 32 ? 2 : 1) : (D == 64 && sizeof(TIn) == 2 ? 4 : 2))
 void fwd_kernel(FwdParams p) {
-  static_assert(!SPARSE || (CAUSAL && kBR == kMaskBlock && 2 * BC == kMaskBlock),
-                "a workgroup is one query block of the mask, two tiles one key block");
+  static_assert(!SPARSE || (CAUSAL && kBR == kMaskBlock && kMaskBlock % BC == 0),
+                "a workgroup is one query block of the mask, whole tiles one key block");
   using LY = Layout<D, BC>;
   // stages 0 and 1 of the K and V tiles (row-major, swizzle rsw)
   __shared__ __attribute__((aligned(1024))) unsigned char k0[LY::kTileBytes];
@@ -106,12 +108,13 @@ void fwd_kernel(FwdParams p) {
   constexpr int kDK = D / 16;   // MFMA steps along d for S^T
   constexpr int kDB = D / 32;   // 32-row blocks of O^T
   constexpr int kKB = BC / 32;  // 32-key blocks of a tile
-  // d = 256: operands are read in chunks (4 steps of S^T, 4 blocks of O^T)
+  // d = 256: operands are read in chunks (4 steps of S^T; 4 blocks of O^T,
+  // 2 with 32-key tiles, whose two waves per SIMD have 256 registers each)
   // so that the staging registers stay within bounds; per-lane offsets are
   // kept for the first 128 columns only (kOffDK steps, kOffDB blocks): the
   // swizzle repeats every 256 bytes of a row (rsw)
   constexpr int kChK = D == 256 ? 4 : kDK;
-  constexpr int kChB = D == 256 ? 4 : kDB;
+  constexpr int kChB = D == 256 ? (BC == 32 ? 2 : 4) : kDB;
   constexpr int kOffDK = kDK < 8 ? kDK : 8;
   constexpr int kOffDB = kDB < 4 ? kDB : 4;
 
@@ -365,18 +368,19 @@ void fwd_kernel(FwdParams p) {
       if (t + 1 < t_end) step(t + 1, k1, v1, k0, v0);
     }
   } else {
-    // Block-sparse kernels: tile t lies in key block t/2 of the mask row of
-    // this query block; the workgroup walks only the tiles of nonzero
-    // blocks, in order, with the same double buffering (tn: the tile after
-    // t, loaded while t is computed).
+    // Block-sparse kernels: tile t lies in key block t / kTilesPerBlock of
+    // the mask row of this query block; the workgroup walks only the tiles
+    // of nonzero blocks, in order, with the same double buffering (tn: the
+    // tile after t, loaded while t is computed).
+    constexpr int kTilesPerBlock = kMaskBlock / BC;
     MaskScan scan;
     scan.stride = 1;
     scan.n = p.nbm;
     scan.reset(p.bmask + (size_t)bh * (size_t)p.bm_stride + (size_t)qb * p.nbm, nullptr);
     auto next_tile = [&](int t) {  // the first tile >= t of a nonzero block, else t_end
       uint32_t fl;
-      const int blk = scan.next(t >> 1, lane, &fl);
-      return blk == (t >> 1) ? t : min(2 * blk, t_end);
+      const int blk = scan.next(t / kTilesPerBlock, lane, &fl);
+      return blk == t / kTilesPerBlock ? t : min(kTilesPerBlock * blk, t_end);
     };
     auto step_to = [&](int t, int tn, const unsigned char* kc, const unsigned char* vc,
                        unsigned char* kn, unsigned char* vn) {
@@ -436,6 +440,10 @@ void fwd_kernel(FwdParams p) {
 }
 
 constexpr int kBC = 64;  // keys per tile
+// d = 256 with bf16 inputs and no block mask: 32 keys per tile, two
+// workgroups per CU (16-18% faster than 64-key tiles at one per CU)
+template <int D, typename TIn>
+constexpr int tile_keys() { return D == 256 && sizeof(TIn) == 2 ? 32 : kBC; }
 // Causal forward launches at d = 128 pair query blocks up to this many blocks
 // per head (N <= 8192): measured 2% faster at N = 4096, 2% slower at N = 32768,
 // where the paired workgroups stream the head's K/V out of step and share
@@ -474,7 +482,7 @@ hipError_t launch_typed(const FwdArgs& a) {
     }
   }
   dim3 grid((unsigned)((long long)p.BH * p.nqb));
-  hipLaunchKernelGGL((fwd_kernel<D, kBC, CAUSAL, TIn, TOut, SPARSE>), grid,
+  hipLaunchKernelGGL((fwd_kernel<D, tile_keys<D, TIn>(), CAUSAL, TIn, TOut, SPARSE>), grid,
                      dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
 }

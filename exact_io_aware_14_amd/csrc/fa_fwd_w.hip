@@ -1,12 +1,13 @@
 // Forward exact attention at head dimension 256: the launches (the kernel
 // and its method are in fa_fwd_kernel.h).
 //
-// Compiled with LLVM's "amdgpu-mfma-vgpr-form" option: a d = 256 wave needs
-// the SIMD's whole register file, and with MFMA results kept in VGPRs where
-// they fit (57 AGPRs instead of 162) the launch takes about 7% less time
-// (0.39 against 0.42 ms at B=4, H=8, N=4096, causal), with bitwise the same
-// results. The d = 64 / 128 forward and the backward kernels are as fast or
-// faster without it, hence the separate file.
+// Compiled with LLVM's "amdgpu-mfma-vgpr-form" option: where a d = 256 wave
+// has the SIMD's whole register file (64-key tiles: fp32 inputs, block-sparse
+// masks), MFMA results kept in VGPRs where they fit (57 AGPRs instead of 162)
+// made the launch about 7% faster (0.39 against 0.42 ms at B=4, H=8, N=4096,
+// causal), with bitwise the same results; the 32-key kernels use no AGPRs
+// either way. The d = 64 / 128 forward and the backward kernels are as fast
+// or faster without it, hence the separate file.
 #include "fa_fwd_kernel.h"
 
 namespace fa {

@@ -111,7 +111,7 @@ static std::pair<long long, long long> keys_of(const Mask& m, int i, int N) {
 
 // ---------------------------------------------------------------- forward
 
-constexpr int kBR = 128, kRW = 32, kBC = 64;
+constexpr int kBR = 128, kRW = 32;
 
 static void check_forward_map(int BH, int group, int N, bool masked, bool pair) {
   const int nqb = (N + kBR - 1) / kBR;
@@ -135,6 +135,7 @@ static void check_forward_map(int BH, int group, int N, bool masked, bool pair) 
           i, seen[i], BH, group, N, masked, pair);
 }
 
+template <int kBC>
 static void check_forward_ranges(int N, const Mask& m) {
   const int nqb = (N + kBR - 1) / kBR;
   const int ntiles = (N + kBC - 1) / kBC;
@@ -308,7 +309,8 @@ int main() {
       masks.push_back(make_mask(true, rand() % 4 == 0 ? -1 : rand() % (N + 64),
                                 rand() % 4 == 0 ? -1 : rand() % (N + 64), N));
     for (const Mask& m : masks) {
-      check_forward_ranges(N, m);
+      check_forward_ranges<64>(N, m);  // 64-key tiles
+      check_forward_ranges<32>(N, m);  // 32-key tiles (d = 256, bf16)
       check_dkdv<128, 64>(N, m, 4, 2);  // d <= 128: 128-key jobs, 64-row tiles, 8 waves
       check_dkdv<128, 32>(N, m, 4, 1);  // d = 256: 128-key jobs, 32-row tiles, 4 waves
       check_dkdv<128, 128, 128>(N, m, 4, 1);  // d = 128: 128-key jobs, 128-row tiles, 4 waves
