@@ -77,9 +77,9 @@ struct FwdParams {
 // to different workgroups and overlap freely. At d = 256 a wave's Q (64
 // registers) and O accumulators (128) leave room for the scores of 32 keys
 // only: bf16 inputs take 32-key tiles (two LDS stages of K and V, 64 KB) at
-// two workgroups per CU, 256 registers per wave; fp32 inputs and
-// block-sparse masks take 64-key tiles at one workgroup per CU (128 KB of
-// stages, the SIMD's whole register file of 512).
+// two workgroups per CU, 256 registers per wave; fp32 inputs take 64-key
+// tiles at one workgroup per CU (128 KB of stages, the SIMD's whole register
+// file of 512).
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
