@@ -18,12 +18,21 @@ missing tile in any head or row of either path shows up in that row.
 The merge runs in fp32 on the GPU from the bf16 partial outputs, so the
 merged O carries one more bf16 rounding than the direct one; the gates
 are those of O and lse against the oracle.
+
+The backward splits the same way. Given the full forward's O and lse, a
+block-sparse backward that sees only the lower (or upper) half of the key
+blocks computes the full dS restricted to those keys (P_ij = exp(S_ij -
+lse_i) and D_i = rowsum(dO_i O_i) do not depend on the mask), so its dQ is
+that half's share of the full dQ, and its dK, dV are the full ones for its
+keys and zero for the others: dQ = dQ_lower + dQ_upper, and likewise dK,
+dV, for every row and key.
 """
 import pytest
 import torch
 
-from exact_io_aware_14_amd import fa_forward, fa_forward_block_sparse, fa_forward_gqa
-from exact_io_aware_14_amd.inputs import MASK_BLOCK, by_name, draw
+from exact_io_aware_14_amd import (fa_backward_block_sparse, fa_backward_gqa, fa_forward,
+                                   fa_forward_block_sparse, fa_forward_gqa)
+from exact_io_aware_14_amd.inputs import MASK_BLOCK, Workload, by_name, draw
 from parity import LSE_MAX_ABS, O_MAX_ABS, O_REL_L2, log
 
 pytestmark = pytest.mark.gpu
@@ -76,3 +85,41 @@ def test_split_keys_merge_to_the_full_output(name, causal):
     assert max_abs <= O_MAX_ABS and rel <= O_REL_L2, (name, max_abs, rel)
     assert lse_abs <= LSE_MAX_ABS, (name, lse_abs)
     assert row_rel <= 2e-2, (name, row_rel)
+
+
+def _check_sum(a, b, full, what):
+    """a + b against the direct result, per head (rel L2 <= 5e-3) and per row
+    (<= 3e-2 of the larger of the row's norm and the head's rms row norm)."""
+    got = a.float() + b.float()
+    ref = full.float()
+    diff = got - ref
+    head_rel = (diff.flatten(2).norm(dim=-1) / ref.flatten(2).norm(dim=-1).clamp_min(1e-30)).max()
+    row_norm = ref.norm(dim=-1)
+    rms_row = row_norm.pow(2).mean(dim=-1, keepdim=True).sqrt()
+    row_rel = (diff.norm(dim=-1) / torch.maximum(row_norm, rms_row).clamp_min(1e-30)).max()
+    log(f"  {what}: head_rel_l2={float(head_rel):.3e} worst_row={float(row_rel):.3e}")
+    assert torch.isfinite(got).all()
+    assert float(head_rel) <= 5e-3 and float(row_rel) <= 3e-2, (what, float(head_rel),
+                                                                 float(row_rel))
+
+
+@pytest.mark.parametrize("name", [
+    "fwdbwd_causal_b4h16n4096d128",   # the bench workload
+    "fwdbwd_causal_b4h8n4096d256",    # d = 256
+    "long_causal_b1h16n16384d128",    # a longer sequence
+])
+def test_split_keys_backward_adds_up(name):
+    if name == "long_causal_b1h16n16384d128":
+        w = Workload(name, 1, 16, 16384, 128, True, True, "bf16", 11)
+    else:
+        w = by_name(name)
+    log(f"case backward split {name}")
+    q, k, v, do = (x.to(DEV) for x in draw(w.shape, w.seed, with_grad=True))
+    o, lse = fa_forward_gqa(q, k, v, scale=w.scale, causal=True)
+    dq, dk, dv = fa_backward_gqa(q, k, v, o, do, lse, scale=w.scale, causal=True)
+    lower, upper = _split_masks(w.N)
+    g1 = fa_backward_block_sparse(q, k, v, o, do, lse, lower, -1, 0, scale=w.scale)
+    g2 = fa_backward_block_sparse(q, k, v, o, do, lse, upper, -1, 0, scale=w.scale)
+    torch.cuda.synchronize()
+    for a, b, full, what in zip(g1, g2, (dq, dk, dv), ("dQ", "dK", "dV")):
+        _check_sum(a, b, full, f"{name} {what}")
