@@ -51,6 +51,7 @@
 
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_schedule.h"
 
 namespace fa {
 namespace {
@@ -339,26 +340,20 @@ __global__ __launch_bounds__(kThreadsF, 2) void fwd_fp8_kernel(Fp8Params p) {
   const int col = lane & 31;
 
   // ---- (head, query block) of this workgroup: as in the bf16 forward
-  int bh, qbr;
-  const int L = blockIdx.x;
-  if (p.xcd_remap) {
-    const int xcd = L & 7, idx = L >> 3, hx = p.BH >> 3;
-    const int g2 = (CAUSAL && hx % 2 == 0) ? 2 : 1;
-    const int grp = idx / (g2 * p.nqb), within = idx % (g2 * p.nqb);
-    const int slot = grp * g2 + within % g2;
-    bh = ((slot / p.group) * 8 + xcd) * p.group + slot % p.group;
-    qbr = within / g2;
-  } else {
-    bh = L % p.BH;
-    qbr = L / p.BH;
-  }
-  const int qb = CAUSAL ? (p.nqb - 1 - qbr) : qbr;
+  // the workgroup's (head, query block) and the key tiles its rows and this
+  // wave's rows walk: the bf16 forward's order and ranges (fa_schedule.h),
+  // without pairs
+  const sched::FwdBlock blk =
+      sched::fwd_block(blockIdx.x, p.BH, p.group, p.nqb, p.xcd_remap != 0, CAUSAL, false);
+  const int bh = blk.bh;
+  const int qb = blk.qb_first;
   const int N = p.N;
   const int kvh = bh / p.group;
-  const int q0 = qb * kRowsF;
-  const int qw0 = q0 + wave * 32;
+  const sched::FwdRange rng =
+      sched::fwd_range<kRowsF, 32, kTileKeys>(qb, wave, N, p.wl, p.wr, CAUSAL);
+  const int qw0 = rng.qw0;
   const int myq = qw0 + col;
-  const int wave_last = min(qw0 + 32, N) - 1;
+  const int wave_last = rng.wave_last;
   // keys this lane's row sees: lo_key .. lo_key + n_vis - 1 (masked kernels:
   // i - wl .. i + wr within 0 .. N-1; otherwise 0 .. N-1)
   const int lo_key = CAUSAL ? myq - p.wl : 0;
@@ -421,11 +416,10 @@ __global__ __launch_bounds__(kThreadsF, 2) void fwd_fp8_kernel(Fp8Params p) {
   f32x16 s[2];
   i32x8 pk;
 
-  const int qlast = min(q0 + kRowsF, N) - 1;
-  const int t_first = CAUSAL ? max(0, q0 - p.wl) / kTileKeys : 0;
-  const int t_end = CAUSAL ? min(N - 1, qlast + p.wr) / kTileKeys + 1 : p.T;
-  const int wt_first = CAUSAL ? max(0, qw0 - p.wl) / kTileKeys : 0;
-  const int wt_end = qw0 >= N ? wt_first : (CAUSAL ? min(N - 1, wave_last + p.wr) / kTileKeys + 1 : p.T);
+  const int t_first = rng.t_first;
+  const int t_end = rng.t_end;
+  const int wt_first = rng.wt_first;
+  const int wt_end = rng.wt_end;
 
   auto fill = [&](int t, unsigned char* kd, unsigned char* vd) {
     const auto kr = make_rsrc(kimg + (size_t)t * kTile, kTile);
@@ -469,8 +463,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void fwd_fp8_kernel(Fp8Params p) {
 
   auto softmax = [&](int t, float ct) {
     const int key0 = t * kTileKeys;
-    const bool need_mask = (key0 + kTileKeys > N) ||
-                           (CAUSAL && (key0 + kTileKeys - 1 > qw0 + p.wr || key0 < wave_last - p.wl));
+    const bool need_mask = sched::fwd_need_mask<kTileKeys>(t, rng, N, p.wl, p.wr, CAUSAL);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
