@@ -24,6 +24,8 @@ bound the arithmetic gives: with u = 2^-8 the unit roundoff of bf16,
 rounding each probability costs at most u * max_j |v_j| and rounding the
 output at most u * |O|, so |O - O_ref| <= u * (|O_ref| + max_j |v_j|) + 1e-3
 (the 1e-3 covers fp32 accumulation), still with the 5e-3 relative L2 gate.
+The random sweep, which draws rows that see only a few keys, uses the tighter
+form of that bound, with P |V| in place of max |v| (check_o_rounding).
 """
 
 from __future__ import annotations
@@ -78,6 +80,56 @@ def check_o_peaked(o, ref, vmax, what):
     max_abs, rel = metrics(o, ref)
     log(f"  {what}: O max_abs={max_abs:.3e} rel_l2={rel:.3e} worst bound margin={-excess:.3e}")
     assert excess <= 0.0 and rel <= O_REL_L2, (what, max_abs, rel, excess)
+
+
+def check_o_rounding(o, ref, pav, what):
+    """Element-wise bound of the forward's rounding, for O of one head.
+
+    The kernels round each probability to bf16 for P.V (|error| <= u p_j)
+    while l sums the unrounded ones, and round O to bf16 (<= u |O|), u = 2^-8;
+    fp32 sums and exponentials add far below 1e-4 at these sizes. So
+    |O_ik - O_ref_ik| <= u (|O_ref_ik| + sum_j P_ij |V_jk|) + 1e-4, with
+    pav = P |V| from the oracle. On rows that average many keys this is about
+    5e-3, tighter than the flat 1e-2; on rows that see a few keys with |O|
+    above about 2.5 the output rounding alone exceeds 1e-2, which no bf16
+    output can meet, and this bound is the gate there. The relative L2 gate
+    of 5e-3 is kept."""
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    o = np.asarray(o, dtype=np.float64)
+    bound = BF16_U * (np.abs(ref) + np.asarray(pav, dtype=np.float64)) + 1e-4
+    excess = float(np.max(np.abs(o - ref) - bound)) if o.size else 0.0
+    max_abs, rel = metrics(o, ref)
+    log(f"  {what}: O max_abs={max_abs:.3e} rel_l2={rel:.3e} worst bound margin={-excess:.3e}")
+    assert excess <= 0.0 and rel <= O_REL_L2, (what, max_abs, rel, excess)
+
+
+def emulate_bf16_forward_head(q, k, v, scale, window, block_mask=None):
+    """The forward's rounding design in fp64 for one head (test model, not
+    the method): P = exp(S - max) over the visible keys, P.V with P rounded
+    to bf16, divided by the unrounded row sum, O rounded to bf16. Rows with no
+    visible key give 0."""
+    import torch
+
+    def bf16(x):
+        return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+    n = q.shape[0]
+    s = (q @ k.T) * scale
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    wl, wr = window
+    vis = np.ones((n, n), dtype=bool)
+    if wl >= 0:
+        vis &= j >= i - wl
+    if wr >= 0:
+        vis &= j <= i + wr
+    if block_mask is not None:
+        vis &= np.asarray(block_mask)[i // oracle.MASK_BLOCK, j // oracle.MASK_BLOCK] != 0
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - np.where(np.isfinite(m), m, 0.0))
+    l = p.sum(axis=1, keepdims=True)
+    return bf16((bf16(p) @ v) / np.where(l > 0, l, 1.0))
 
 
 def check_lse(lse, ref, what):

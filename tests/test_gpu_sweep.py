@@ -3,7 +3,14 @@
 so that combinations the hand-picked cases leave out are covered too. Each case
 runs the forward and the backward through the window calls (which also take the
 causal mask (-1, 0) and no mask (-1, -1)) and compares every head with the fp64
-oracle."""
+oracle.
+
+The draw includes rows that see only a few keys (short sequences, narrow
+windows, sparse masks). Where such a row's |O| exceeds about 2.5, rounding O to
+bf16 alone can move it by more than the flat 1e-2, so O is gated here by the
+element-wise bound of the forward's rounding (parity.check_o_rounding), which
+is tighter than 1e-2 on rows that average many keys, with the same relative L2
+gate."""
 
 from __future__ import annotations
 
@@ -16,7 +23,7 @@ import torch
 import oracle
 from exact_io_aware_14_amd import fa_backward_window, fa_forward_window
 from exact_io_aware_14_amd.inputs import draw, to_f64
-from parity import check_grad, check_lse, check_o, dq_allowances, log
+from parity import check_grad, check_lse, check_o_rounding, dq_allowances, log
 
 pytestmark = pytest.mark.gpu
 
@@ -63,13 +70,14 @@ def test_sweep_forward_backward(case):
 
     qf, kf, vf, dof = (to_f64(x) for x in (q, k, v, do))
     ro, rl = oracle.forward(qf, kf, vf, scale, window)
+    pav, _ = oracle.forward(qf, kf, np.abs(vf), scale, window)  # P |V|
     rq, rk, rv = oracle.backward(qf, kf, vf, dof, scale, window)
     aq = dq_allowances(qf, kf, vf, dof, scale, window)
     o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
     dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
     for b in range(B):
         for h in range(H):
-            check_o(o[b, h], ro[b, h], f"{case} b={b} h={h}")
+            check_o_rounding(o[b, h], ro[b, h], pav[b, h], f"{case} b={b} h={h}")
             check_lse(lse[b, h], rl[b, h], f"{case} b={b} h={h}")
             check_grad(dq[b, h], rq[b, h], f"{case} b={b} h={h} dQ", allow=aq[b, h])
         for g in range(Hkv):
@@ -122,13 +130,14 @@ def test_sweep_block_sparse(case):
         for h in range(H):
             g = oracle.kv_head(h, H, Hkv)
             hm = bm_np if shared else bm_np[b, h]
-            ro, rl = oracle.forward_head(to_f64(q[b, h]), to_f64(k[b, g]), to_f64(v[b, g]), scale,
-                                         window, block_mask=hm)
+            qh, kh, vh = to_f64(q[b, h]), to_f64(k[b, g]), to_f64(v[b, g])
+            ro, rl = oracle.forward_head(qh, kh, vh, scale, window, block_mask=hm)
+            pav, _ = oracle.forward_head(qh, kh, np.abs(vh), scale, window, block_mask=hm)
             what = f"{case} b={b} h={h}"
             empty = np.isneginf(rl)
             assert np.array_equal(np.isneginf(lse[b, h]), empty), what
             assert np.all(o[b, h][empty] == 0.0), what
-            check_o(o[b, h], ro, what)
+            check_o_rounding(o[b, h], ro, pav, what)
             if (~empty).any():
                 check_lse(lse[b, h][~empty], rl[~empty], what)
             check_grad(dq[b, h], rq[b, h], what + " dQ", allow=aq[b, h])
