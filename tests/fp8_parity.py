@@ -27,7 +27,12 @@ requires the GPU output to lie within that allowance of the oracle's:
 
 Bound per element: |O - O_ref| <= 2^-8 |O_ref| (bf16 output rounding) +
 sum_j (flip_ij + 2 dP_ij) |V~_jc| / l_i + 1e-3 (fp32 accumulation), with
-relative L2 error <= 5e-3 over the head as for the bf16 forward.
+relative L2 error <= 5e-3 over the head as for the bf16 forward, counted on
+what the ambiguous decisions do not explain: per element, the error less its
+allowance for flips and score shifts (the flip_ij and dP_ij terms). Either
+neighbour of an ambiguous midpoint is a correct rounding, and one flip of a
+row's dominant probability moves that row by one e4m3 step of P (1/16 of
+2^8 P in [128, 256)), which on a head of a few dozen rows alone exceeds 5e-3.
 """
 
 from __future__ import annotations
@@ -96,17 +101,21 @@ def fp8_allowance(q, k, v, scale, causal, signs):
     dp = p * np.expm1(ds)
     extra = ((flip * (hi - lo) / 256.0 + 2.0 * dp) @ av) / l
     bound = 2.0 ** -8 * np.abs(ro) + extra + 1e-3
-    return ro, rl, bound, int(flip.sum())
+    return ro, rl, bound, extra, int(flip.sum())
 
 
 def check_fp8_o(o, q, k, v, scale, causal, signs, what):
     """O of the FP8 path against the oracle with the allowance above; returns lse_ref."""
     assert np.all(np.isfinite(o)), f"{what}: non-finite output"
-    ro, rl, bound, flips = fp8_allowance(q, k, v, scale, causal, signs)
+    ro, rl, bound, ambiguous, flips = fp8_allowance(q, k, v, scale, causal, signs)
     o = np.asarray(o, dtype=np.float64)
     excess = float(np.max(np.abs(o - ro) - bound))
     max_abs, rel = metrics(o, ro)
-    log(f"  {what}: O max_abs={max_abs:.3e} rel_l2={rel:.3e} ambiguous P={flips} "
-        f"worst bound margin={-excess:.3e}")
-    assert excess <= 0.0 and rel <= O_REL_L2, (what, max_abs, rel, excess)
+    # the relative L2 of what the ambiguous decisions do not explain
+    rest = np.maximum(np.abs(o - ro) - ambiguous, 0.0)
+    denom = float(np.linalg.norm(ro))
+    rel_rest = float(np.linalg.norm(rest)) / denom if denom > 0 else float(np.linalg.norm(rest))
+    log(f"  {what}: O max_abs={max_abs:.3e} rel_l2={rel:.3e} (without ambiguous decisions "
+        f"{rel_rest:.3e}) ambiguous P={flips} worst bound margin={-excess:.3e}")
+    assert excess <= 0.0 and rel_rest <= O_REL_L2, (what, max_abs, rel, rel_rest, excess)
     return rl
