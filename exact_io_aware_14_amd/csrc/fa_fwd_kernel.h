@@ -248,7 +248,10 @@ void fwd_kernel(FwdParams p) {
     }
   };
 
-  // MFMA phase, second half: S^T = K Q^T for the K tile ks
+  // MFMA phase, second half: S^T = K Q^T for the K tile ks. At d = 64 and
+  // 128 the K reads run four ahead of the MFMAs that use them (1-2% faster
+  // at d = 128 than issuing every read first; the same at d = 64); at
+  // d = 256 each chunk's reads come first.
   auto qk = [&](const unsigned char* ks) {
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) s[kb] = zero16();
@@ -264,8 +267,20 @@ void fwd_kernel(FwdParams p) {
       for (int kk = 0; kk < kChK; ++kk)
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb) s[kb] = mfma32(a[kk][kb], qreg[c0 + kk], s[kb]);
-      __builtin_amdgcn_sched_group_barrier(0x100, kChK * kKB, 0);  // the LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, kChK * kKB, 0);  // then the MFMAs
+      constexpr int kN = kChK * kKB;  // reads and MFMAs of the chunk
+      constexpr int kAhead = 4;
+      if constexpr (D != 256 && kN > kAhead) {
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // the first reads
+#pragma unroll
+        for (int i = 0; i < kN - kAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // an MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);  // the last MFMAs
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x100, kN, 0);  // the LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, kN, 0);  // then the MFMAs
+      }
     }
   };
 
