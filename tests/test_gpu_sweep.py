@@ -53,7 +53,12 @@ def _draw_cases(n, seed):
     return cases
 
 
-CASES = _draw_cases(32, seed=20261203)
+CASES = _draw_cases(32, seed=20261203) + [
+    # from a longer run of this draw: row 1 of head (1, 0) sees two keys with
+    # |O| about 4, where bf16 rounding leaves O 1.49e-2 from the oracle (above
+    # the flat 1e-2, inside the element-wise bound)
+    (2, 2, 1, 62, 128, (-1, 0)),
+]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{i}-{c}" for i, c in enumerate(CASES)])
