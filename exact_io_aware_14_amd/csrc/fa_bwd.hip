@@ -451,7 +451,6 @@ __device__ __forceinline__ void dq_job(const BwdParams& p, int bh, int qblk,
 
   // the job's rows, this wave's rows and the key tiles they walk
   const sched::DqRange rng = sched::dq_range<kQBlock, kTile>(qblk, wave, N, p.wl, p.wr, CAUSAL);
-  const int q0 = rng.q0;
   const int qw0 = rng.qw0;
   const int myq = qw0 + col;
 

@@ -338,10 +338,8 @@ __device__ __forceinline__ void dq_job_w(const BwdParams& p, int bh, int qblk,
   // the job's rows, this wave's rows and the key tiles they walk
   const sched::DqRange rng =
       sched::dq_range<kQBlockW, kKTileW>(qblk, wave, N, p.wl, p.wr, CAUSAL);
-  const int q0 = rng.q0;
   const int qw0 = rng.qw0;
   const int myq = qw0 + col;
-  const int wave_last = rng.wave_last;
 
   OffsetsW<D> off;
   off.init(lane);

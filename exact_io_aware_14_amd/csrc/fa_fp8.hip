@@ -353,7 +353,6 @@ __global__ __launch_bounds__(kThreadsF, 2) void fwd_fp8_kernel(Fp8Params p) {
       sched::fwd_range<kRowsF, 32, kTileKeys>(qb, wave, N, p.wl, p.wr, CAUSAL);
   const int qw0 = rng.qw0;
   const int myq = qw0 + col;
-  const int wave_last = rng.wave_last;
   // keys this lane's row sees: lo_key .. lo_key + n_vis - 1 (masked kernels:
   // i - wl .. i + wr within 0 .. N-1; otherwise 0 .. N-1)
   const int lo_key = CAUSAL ? myq - p.wl : 0;

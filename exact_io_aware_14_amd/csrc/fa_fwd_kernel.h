@@ -149,10 +149,8 @@ void fwd_kernel(FwdParams p) {
   // rows of the block and of this wave, and the key tiles they walk
   const sched::FwdRange rng =
       sched::fwd_range<kBR, kRowsPerWave, BC>(qb, wave, N, p.wl, p.wr, CAUSAL);
-  const int q0 = rng.q0;                // first row of the block
-  const int qw0 = rng.qw0;              // this wave's
+  const int qw0 = rng.qw0;              // first row of this wave
   const int myq = qw0 + col;            // this lane's row
-  const int wave_last = rng.wave_last;
   // keys this lane's row sees: lo_key .. lo_key + n_vis - 1 (masked kernels:
   // i - wl .. i + wr within 0 .. N-1; otherwise 0 .. N-1)
   const int lo_key = CAUSAL ? myq - p.wl : 0;
